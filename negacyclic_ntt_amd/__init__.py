@@ -12,7 +12,7 @@ from . import inputs, workloads  # noqa: F401  (pure Python, no GPU needed)
 def __getattr__(name):
     # The binding loads the shared library on first use, so that importing the
     # package (e.g. for `inputs`) does not require a GPU or a built library.
-    if name.startswith("__"):
+    if name.startswith("__") or name in ("binding", "build"):
         raise AttributeError(name)
-    from . import binding
-    return getattr(binding, name)
+    import importlib
+    return getattr(importlib.import_module(__name__ + ".binding"), name)

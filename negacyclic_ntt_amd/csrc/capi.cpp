@@ -1,0 +1,123 @@
+// C-ABI entry points: argument validation (before anything is enqueued), device
+// selection and dispatch to the launchers.  Follows the FHElium native-call
+// conventions ("Eager, Compile, and native execution", sections "Schema
+// registration and device dispatch" and "CUDA execution"): shapes, ranges and
+// forbidden overlap are checked first; work goes on the caller's stream with no
+// host synchronisation; launch failures are reported, asynchronous faults surface
+// at the caller's next synchronisation.
+#include "internal.h"
+
+using namespace nntt;
+
+namespace {
+
+constexpr uint64_t kMaxElements = 1ull << 36;  // 512 GiB of residues: beyond any device
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Half-open byte ranges [a, a + na) and [b, b + nb).
+bool overlaps(const void* a, uint64_t na, const void* b, uint64_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return na && nb && x < y + nb && y < x + na;
+}
+
+// out may equal `in` exactly (if allowed) but may not overlap it otherwise.
+bool bad_overlap(const void* out, const void* in, uint64_t bytes, bool exact_ok) {
+  if (out == in) return !exact_ok && bytes != 0;
+  return overlaps(out, bytes, in, bytes);
+}
+
+int check_plan_range(const ntt_plan* p, uint64_t batch, uint32_t limb_begin, uint32_t num_limbs,
+                     uint64_t components, uint64_t* elements) {
+  if (!p) return NTT_EINVAL;
+  if (p->device < 0) return NTT_EDEVICE;
+  if (num_limbs == 0 || limb_begin >= p->num_primes || num_limbs > p->num_primes - limb_begin) return NTT_EINVAL;
+  const uint64_t per = (uint64_t)num_limbs * p->n * components;
+  if (batch > kMaxElements / per) return NTT_EUNSUPPORTED;
+  *elements = batch * per;
+  return NTT_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? NTT_OK : NTT_EDEVICE; }
+
+int transform(const ntt_plan* p, uint64_t* data, uint64_t batch, uint32_t limb_begin, uint32_t num_limbs,
+              void* stream, bool inverse) {
+  uint64_t elems = 0;
+  int rc = check_plan_range(p, batch, limb_begin, num_limbs, 1, &elems);
+  if (rc) return rc;
+  if (!elems) return NTT_OK;
+  if (!data || !aligned16(data)) return NTT_EINVAL;
+  DeviceGuard g(p->device);
+  if (!g.ok) return NTT_EDEVICE;
+  return status_of(launch_ntt(p, data, batch, limb_begin, num_limbs, inverse, (hipStream_t)stream));
+}
+
+bool valid_galois(const ntt_plan* p, uint64_t g) { return (g & 1) && g < 2ull * p->n; }
+
+}  // namespace
+
+extern "C" int ntt_forward(const ntt_plan* p, uint64_t* data, uint64_t batch, uint32_t limb_begin,
+                           uint32_t num_limbs, void* stream) {
+  return transform(p, data, batch, limb_begin, num_limbs, stream, false);
+}
+
+extern "C" int ntt_inverse(const ntt_plan* p, uint64_t* data, uint64_t batch, uint32_t limb_begin,
+                           uint32_t num_limbs, void* stream) {
+  return transform(p, data, batch, limb_begin, num_limbs, stream, true);
+}
+
+extern "C" int ntt_forward_galois(const ntt_plan* p, uint64_t* out, const uint64_t* in, uint64_t galois_elt,
+                                  uint64_t batch, uint32_t limb_begin, uint32_t num_limbs, void* stream) {
+  uint64_t elems = 0;
+  int rc = check_plan_range(p, batch, limb_begin, num_limbs, 1, &elems);
+  if (rc) return rc;
+  if (!valid_galois(p, galois_elt)) return NTT_EINVAL;
+  if (!elems) return NTT_OK;
+  if (!out || !in || !aligned16(out) || !aligned16(in)) return NTT_EINVAL;
+  if (bad_overlap(out, in, elems * 8, true)) return NTT_EOVERLAP;
+  DeviceGuard g(p->device);
+  if (!g.ok) return NTT_EDEVICE;
+  return status_of(launch_ntt_galois(p, out, in, galois_elt, batch, limb_begin, num_limbs, (hipStream_t)stream));
+}
+
+extern "C" int poly_mul_ntt(const ntt_plan* p, uint64_t* out, const uint64_t* a, const uint64_t* b, uint64_t batch,
+                            uint32_t limb_begin, uint32_t num_limbs, void* stream) {
+  uint64_t elems = 0;
+  int rc = check_plan_range(p, batch, limb_begin, num_limbs, 1, &elems);
+  if (rc) return rc;
+  if (!elems) return NTT_OK;
+  if (!out || !a || !b || !aligned16(out) || !aligned16(a) || !aligned16(b)) return NTT_EINVAL;
+  if (bad_overlap(out, a, elems * 8, true) || bad_overlap(out, b, elems * 8, true)) return NTT_EOVERLAP;
+  DeviceGuard g(p->device);
+  if (!g.ok) return NTT_EDEVICE;
+  return status_of(launch_pointwise(p, out, a, b, batch, limb_begin, num_limbs, (hipStream_t)stream));
+}
+
+extern "C" int ct_tensor_ntt(const ntt_plan* p, uint64_t* out, const uint64_t* a, const uint64_t* b, uint64_t batch,
+                             uint32_t limb_begin, uint32_t num_limbs, void* stream) {
+  uint64_t elems = 0;
+  int rc = check_plan_range(p, batch, limb_begin, num_limbs, 3, &elems);
+  if (rc) return rc;
+  if (!elems) return NTT_OK;
+  if (!out || !a || !b || !aligned16(out) || !aligned16(a) || !aligned16(b)) return NTT_EINVAL;
+  const uint64_t in_bytes = elems / 3 * 2 * 8, out_bytes = elems * 8;
+  if (overlaps(out, out_bytes, a, in_bytes) || overlaps(out, out_bytes, b, in_bytes)) return NTT_EOVERLAP;
+  DeviceGuard g(p->device);
+  if (!g.ok) return NTT_EDEVICE;
+  return status_of(launch_tensor(p, out, a, b, batch, limb_begin, num_limbs, (hipStream_t)stream));
+}
+
+extern "C" int automorph(const ntt_plan* p, uint64_t* out, const uint64_t* in, uint64_t galois_elt, int domain,
+                         uint64_t batch, uint32_t limb_begin, uint32_t num_limbs, void* stream) {
+  uint64_t elems = 0;
+  int rc = check_plan_range(p, batch, limb_begin, num_limbs, 1, &elems);
+  if (rc) return rc;
+  if (!valid_galois(p, galois_elt) || (domain != 0 && domain != 1)) return NTT_EINVAL;
+  if (!elems) return NTT_OK;
+  if (!out || !in || !aligned16(out) || !aligned16(in)) return NTT_EINVAL;
+  if (overlaps(out, elems * 8, in, elems * 8)) return NTT_EOVERLAP;
+  DeviceGuard g(p->device);
+  if (!g.ok) return NTT_EDEVICE;
+  return status_of(launch_automorph(p, out, in, galois_elt, domain, batch, limb_begin, num_limbs,
+                                    (hipStream_t)stream));
+}

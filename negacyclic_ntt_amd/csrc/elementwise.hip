@@ -1,0 +1,157 @@
+// Element-wise kernels: pointwise products, the ciphertext tensor product and the
+// Galois automorphisms.  All are bound by HBM traffic, so each thread moves 16-byte
+// vectors and the arithmetic (Barrett products) is off the critical path.
+//
+// FHElium ("Eager, Compile, and native execution", section "CUDA execution")
+// maps kernel grids onto the tensor axes limb x coefficient tile x batch; here the
+// [batch][limb][n] tensor is treated as one flat array whose row r has limb
+// r % num_limbs, which covers the same axes with a 1-D grid.
+#include "internal.h"
+
+namespace nntt {
+namespace {
+
+constexpr int kThreads = 256;
+
+// Blocks are dispatched round-robin over the 8 XCDs of an MI355X; this maps the
+// hardware block id to a logical id so that each XCD works on one contiguous
+// range of logical blocks (and hence of the tensor), keeping its L2 working set
+// local.  Identity for the tail that does not fill all eight.
+__device__ __forceinline__ uint32_t xcd_local_block(uint32_t b, uint32_t nblocks) {
+  constexpr uint32_t kXcd = 8;
+  const uint32_t full = nblocks - nblocks % kXcd;
+  if (b >= full) return b;
+  return (b % kXcd) * (full / kXcd) + b / kXcd;
+}
+
+__global__ __launch_bounds__(kThreads) void pointwise_kernel(uint64_t* __restrict__ out,
+                                                             const uint64_t* __restrict__ a,
+                                                             const uint64_t* __restrict__ b,
+                                                             const ModInfo* __restrict__ mods, uint32_t logn,
+                                                             uint32_t num_limbs, uint32_t limb_begin,
+                                                             uint64_t pairs) {
+  const uint64_t p = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (p >= pairs) return;
+  const uint64_t e = 2 * p;
+  const Barrett br = mods[limb_begin + (uint32_t)((e >> logn) % num_limbs)].br;
+  const ulonglong2 x = *reinterpret_cast<const ulonglong2*>(a + e);
+  const ulonglong2 y = *reinterpret_cast<const ulonglong2*>(b + e);
+  ulonglong2 z;
+  z.x = barrett_mul(x.x, y.x, br);
+  z.y = barrett_mul(x.y, y.y, br);
+  *reinterpret_cast<ulonglong2*>(out + e) = z;
+}
+
+// a, b: [batch][2][L][n]; out: [batch][3][L][n].
+__global__ __launch_bounds__(kThreads) void tensor_kernel(uint64_t* __restrict__ out,
+                                                          const uint64_t* __restrict__ a,
+                                                          const uint64_t* __restrict__ b,
+                                                          const ModInfo* __restrict__ mods, uint32_t logn,
+                                                          uint32_t num_limbs, uint32_t limb_begin,
+                                                          uint64_t pairs) {
+  const uint64_t p = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (p >= pairs) return;
+  const uint64_t plane = (uint64_t)num_limbs << logn;  // elements per component
+  const uint64_t e = 2 * p;                            // flat index in [batch][L][n]
+  const uint64_t bi = e / plane, off = e % plane;
+  const Barrett br = mods[limb_begin + (uint32_t)(off >> logn)].br;
+  const uint64_t q = br.q;
+  const uint64_t* a0 = a + bi * 2 * plane + off;
+  const uint64_t* b0 = b + bi * 2 * plane + off;
+  uint64_t* d0 = out + bi * 3 * plane + off;
+  const ulonglong2 x0 = *reinterpret_cast<const ulonglong2*>(a0);
+  const ulonglong2 x1 = *reinterpret_cast<const ulonglong2*>(a0 + plane);
+  const ulonglong2 y0 = *reinterpret_cast<const ulonglong2*>(b0);
+  const ulonglong2 y1 = *reinterpret_cast<const ulonglong2*>(b0 + plane);
+  ulonglong2 r0, r1, r2;
+  r0.x = barrett_mul(x0.x, y0.x, br);
+  r0.y = barrett_mul(x0.y, y0.y, br);
+  r1.x = add_mod(barrett_mul(x0.x, y1.x, br), barrett_mul(x1.x, y0.x, br), q);
+  r1.y = add_mod(barrett_mul(x0.y, y1.y, br), barrett_mul(x1.y, y0.y, br), q);
+  r2.x = barrett_mul(x1.x, y1.x, br);
+  r2.y = barrett_mul(x1.y, y1.y, br);
+  *reinterpret_cast<ulonglong2*>(d0) = r0;
+  *reinterpret_cast<ulonglong2*>(d0 + plane) = r1;
+  *reinterpret_cast<ulonglong2*>(d0 + 2 * plane) = r2;
+}
+
+// Coefficient domain: out[e] = in[i] if i < n else -in[i - n], i = e * h mod 2n,
+// h = g^-1 mod 2n (the inverse of the scatter i -> i g).  Gather form: writes are
+// coalesced, reads hit L2 thanks to the XCD-local block order.
+__global__ __launch_bounds__(kThreads) void automorph_coeff_kernel(uint64_t* __restrict__ out,
+                                                                   const uint64_t* __restrict__ in,
+                                                                   const ModInfo* __restrict__ mods,
+                                                                   uint32_t logn, uint32_t h,
+                                                                   uint32_t num_limbs, uint32_t limb_begin,
+                                                                   uint64_t total) {
+  const uint32_t lb = xcd_local_block(blockIdx.x, gridDim.x);
+  const uint64_t idx = (uint64_t)lb * kThreads + threadIdx.x;
+  if (idx >= total) return;
+  const uint32_t n = 1u << logn, mask2n = 2 * n - 1;
+  const uint64_t row = idx >> logn;
+  const uint32_t e = (uint32_t)(idx & (n - 1));
+  const uint32_t i = (uint32_t)(((uint64_t)e * h) & mask2n);
+  const uint64_t q = mods[limb_begin + (uint32_t)(row % num_limbs)].q;
+  const uint64_t* src = in + (row << logn);
+  uint64_t v;
+  if (i < n)
+    v = src[i];
+  else
+    v = neg_mod(src[i - n], q);
+  out[idx] = v;
+}
+
+// NTT domain (bit-reversed slots): out[k] = in[p(k)], 2 brv(p) + 1 = (2 brv(k) + 1) g mod 2n.
+__global__ __launch_bounds__(kThreads) void automorph_ntt_kernel(uint64_t* __restrict__ out,
+                                                                 const uint64_t* __restrict__ in, uint32_t logn,
+                                                                 uint32_t g, uint64_t total) {
+  const uint64_t idx = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= total) return;
+  const uint32_t n = 1u << logn;
+  const uint64_t row = idx >> logn;
+  const uint32_t k = (uint32_t)(idx & (n - 1));
+  const uint32_t bk = __brev(k) >> (32 - logn);
+  const uint32_t e = (uint32_t)(((uint64_t)(2 * bk + 1) * g) & (2 * n - 1));
+  const uint32_t p = __brev((e - 1) >> 1) >> (32 - logn);
+  out[idx] = in[(row << logn) + p];
+}
+
+uint32_t blocks_for(uint64_t work) { return (uint32_t)((work + kThreads - 1) / kThreads); }
+
+}  // namespace
+
+hipError_t launch_pointwise(const ntt_plan* p, uint64_t* out, const uint64_t* a, const uint64_t* b, uint64_t batch,
+                            uint32_t limb_begin, uint32_t num_limbs, hipStream_t s) {
+  const uint64_t pairs = (batch * num_limbs * p->n) / 2;
+  if (!pairs) return hipSuccess;
+  hipLaunchKernelGGL(pointwise_kernel, dim3(blocks_for(pairs)), dim3(kThreads), 0, s, out, a, b, p->d_mods, p->logn,
+                     num_limbs, limb_begin, pairs);
+  return hipGetLastError();
+}
+
+hipError_t launch_tensor(const ntt_plan* p, uint64_t* out, const uint64_t* a, const uint64_t* b, uint64_t batch,
+                         uint32_t limb_begin, uint32_t num_limbs, hipStream_t s) {
+  const uint64_t pairs = (batch * num_limbs * p->n) / 2;
+  if (!pairs) return hipSuccess;
+  hipLaunchKernelGGL(tensor_kernel, dim3(blocks_for(pairs)), dim3(kThreads), 0, s, out, a, b, p->d_mods, p->logn,
+                     num_limbs, limb_begin, pairs);
+  return hipGetLastError();
+}
+
+hipError_t launch_automorph(const ntt_plan* p, uint64_t* out, const uint64_t* in, uint64_t g, int domain,
+                            uint64_t batch, uint32_t limb_begin, uint32_t num_limbs, hipStream_t s) {
+  const uint64_t total = batch * num_limbs * p->n;
+  if (!total) return hipSuccess;
+  const uint32_t two_n = 2 * p->n;
+  if (domain == 0) {
+    const uint32_t h = (uint32_t)host_invmod(g % two_n, two_n);
+    hipLaunchKernelGGL(automorph_coeff_kernel, dim3(blocks_for(total)), dim3(kThreads), 0, s, out, in, p->d_mods,
+                       p->logn, h, num_limbs, limb_begin, total);
+  } else {
+    hipLaunchKernelGGL(automorph_ntt_kernel, dim3(blocks_for(total)), dim3(kThreads), 0, s, out, in, p->logn,
+                       (uint32_t)(g % two_n), total);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace nntt

@@ -1,0 +1,75 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "modarith.h"
+#include "negacyclic_ntt.h"
+
+namespace nntt {
+
+// Per-prime constants, device resident (one entry per plan prime).
+struct ModInfo {
+  uint64_t q;
+  uint64_t n_inv, n_inv_shoup;  // n^-1 mod q and floor(n^-1 * 2^64 / q)
+  uint32_t n_inv32, n_inv_shoup32;  // narrow (q < 2^30) Shoup pair, else 0
+  Barrett br;
+};
+
+constexpr uint32_t kMaxLogN = 16;
+constexpr uint32_t kMaxPrimes = 4096;
+
+}  // namespace nntt
+
+struct ntt_plan {
+  uint32_t n = 0, logn = 0, num_primes = 0;
+  int device = -1;
+  std::vector<uint64_t> primes, psis;
+  std::vector<uint8_t> narrow;                   // 1 if q < 2^30
+  std::vector<uint64_t> h_fwd, h_fwd_sh, h_inv, h_inv_sh;  // host tables [L][n]
+  std::vector<nntt::ModInfo> h_mods;
+  // device copies
+  nntt::Wide::Tw* d_fwd = nullptr;    // [L][n] {psi^brv(k), shoup}
+  nntt::Wide::Tw* d_inv = nullptr;    // [L][n] {psi^-brv(k), shoup}
+  nntt::Narrow::Tw* d_fwd32 = nullptr;  // [L][n], entries of wide primes are zero
+  nntt::Narrow::Tw* d_inv32 = nullptr;
+  nntt::ModInfo* d_mods = nullptr;    // [L]
+};
+
+namespace nntt {
+
+// Host helpers (plan.cpp)
+uint64_t host_mulmod(uint64_t a, uint64_t b, uint64_t q);
+uint64_t host_powmod(uint64_t b, uint64_t e, uint64_t q);
+uint64_t host_invmod(uint64_t a, uint64_t q);
+bool host_is_prime(uint64_t n);
+Barrett host_barrett(uint64_t q);
+
+// RAII device selection: makes `dev` current and restores the previous device.
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = false;
+  explicit DeviceGuard(int dev);
+  ~DeviceGuard();
+};
+
+// Launchers (ntt.hip). Arguments already validated. Return the launch status.
+hipError_t launch_ntt(const ntt_plan* p, uint64_t* data, uint64_t batch, uint32_t limb_begin, uint32_t num_limbs,
+                      bool inverse, hipStream_t s);
+hipError_t launch_ntt_galois(const ntt_plan* p, uint64_t* out, const uint64_t* in, uint64_t g, uint64_t batch,
+                             uint32_t limb_begin, uint32_t num_limbs, hipStream_t s);
+// True when every prime in [limb_begin, limb_begin + num_limbs) is below 2^30.
+bool range_is_narrow(const ntt_plan* p, uint32_t limb_begin, uint32_t num_limbs);
+
+// Element-wise launchers (elementwise.hip).
+hipError_t launch_pointwise(const ntt_plan* p, uint64_t* out, const uint64_t* a, const uint64_t* b, uint64_t batch,
+                            uint32_t limb_begin, uint32_t num_limbs, hipStream_t s);
+hipError_t launch_tensor(const ntt_plan* p, uint64_t* out, const uint64_t* a, const uint64_t* b, uint64_t batch,
+                         uint32_t limb_begin, uint32_t num_limbs, hipStream_t s);
+hipError_t launch_automorph(const ntt_plan* p, uint64_t* out, const uint64_t* in, uint64_t g, int domain,
+                            uint64_t batch, uint32_t limb_begin, uint32_t num_limbs, hipStream_t s);
+
+}  // namespace nntt

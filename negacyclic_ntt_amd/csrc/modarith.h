@@ -1,0 +1,112 @@
+// Device-side modular arithmetic for gfx950.
+//
+// Two residue widths share one set of kernels through the traits below:
+//   Wide   : q < 2^62, residues in uint64_t.  Lazy (Harvey) butterflies keep
+//            values in [0, 4q) < 2^64.  Products by a table constant use Shoup's
+//            method with w' = floor(w * 2^64 / q).
+//   Narrow : q < 2^30, residues in uint32_t (stored as uint64_t in memory),
+//            [0, 4q) < 2^32, Shoup with w' = floor(w * 2^32 / q).
+// Products of two variables (pointwise, tensor, key inner product) use Barrett
+// reduction of the 128-bit product (see barrett_mul).
+//
+// CDNA4 issues v_mul_lo_u32 / v_mul_hi_u32 / v_mad_u64_u32 at full rate, so a
+// Shoup product is ~16-19 VALU instructions and a lazy butterfly ~26.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nntt {
+
+struct Wide {
+  using T = uint64_t;
+  struct Tw {
+    uint64_t w, wp;
+  };
+  static constexpr int kPadShift = 4;  // one pad slot per 16 elements (128 B of LDS banks)
+
+  // y * w mod q, result in [0, 2q); any y < 2^64.
+  static __device__ __forceinline__ T mul(T y, Tw t, T q) {
+    uint64_t hi = __umul64hi(y, t.wp);
+    return y * t.w - hi * q;
+  }
+  static __device__ __forceinline__ T load(const uint64_t* p) { return *p; }
+  static __device__ __forceinline__ uint64_t widen(T x) { return x; }
+};
+
+struct Narrow {
+  using T = uint32_t;
+  struct Tw {
+    uint32_t w, wp;
+  };
+  static constexpr int kPadShift = 5;  // one pad slot per 32 elements
+
+  static __device__ __forceinline__ T mul(T y, Tw t, T q) {
+    uint32_t hi = __umulhi(y, t.wp);
+    return y * t.w - hi * q;
+  }
+  static __device__ __forceinline__ uint64_t widen(T x) { return x; }
+};
+
+// x in [0, 2m) -> [0, m)
+template <class T>
+__device__ __forceinline__ T csub(T x, T m) {
+  return x >= m ? x - m : x;
+}
+
+// Cooley-Tukey (decimation in time) butterfly with lazy reduction.
+// In: x, y in [0, 4q).  Out: x + w y, x - w y + 2q, both in [0, 4q).
+template <class A>
+__device__ __forceinline__ void ct_butterfly(typename A::T& x, typename A::T& y, typename A::Tw w, typename A::T q,
+                                             typename A::T two_q) {
+  using T = typename A::T;
+  T u = csub(x, two_q);
+  T t = A::mul(y, w, q);
+  x = u + t;
+  y = u - t + two_q;
+}
+
+// Gentleman-Sande (decimation in frequency) butterfly with lazy reduction.
+// In: x, y in [0, 2q).  Out: x + y, (x - y) w, both in [0, 2q).
+template <class A>
+__device__ __forceinline__ void gs_butterfly(typename A::T& x, typename A::T& y, typename A::Tw w, typename A::T q,
+                                             typename A::T two_q) {
+  using T = typename A::T;
+  T s = x + y;
+  T d = x - y + two_q;
+  x = csub(s, two_q);
+  y = A::mul(d, w, q);
+}
+
+// Barrett reduction of a full product of two canonical 64-bit residues.
+// q < 2^62 with k = bitlen(q); mu = floor(2^(2k) / q) < 2^63.
+// q1 = floor(x / 2^(k-1)), q3 = floor(q1 * mu / 2^(k+1)); then
+// floor(x/q) - 2 <= q3 <= floor(x/q), so x - q3 q lies in [0, 3q).
+struct Barrett {
+  uint64_t q, mu;
+  uint32_t k;
+};
+
+__device__ __forceinline__ uint64_t shr128(uint64_t hi, uint64_t lo, uint32_t s) {
+  // s in [1, 63]
+  return (hi << (64 - s)) | (lo >> s);
+}
+
+__device__ __forceinline__ uint64_t barrett_reduce(uint64_t hi, uint64_t lo, const Barrett& b) {
+  uint64_t q1 = shr128(hi, lo, b.k - 1);
+  uint64_t ph = __umul64hi(q1, b.mu), pl = q1 * b.mu;
+  uint64_t q3 = shr128(ph, pl, b.k + 1);
+  uint64_t r = lo - q3 * b.q;
+  r = csub(r, b.q);
+  r = csub(r, b.q);
+  return r;
+}
+
+__device__ __forceinline__ uint64_t barrett_mul(uint64_t a, uint64_t c, const Barrett& b) {
+  return barrett_reduce(__umul64hi(a, c), a * c, b);
+}
+
+__device__ __forceinline__ uint64_t add_mod(uint64_t a, uint64_t c, uint64_t q) { return csub(a + c, q); }
+__device__ __forceinline__ uint64_t sub_mod(uint64_t a, uint64_t c, uint64_t q) { return a >= c ? a - c : a + q - c; }
+__device__ __forceinline__ uint64_t neg_mod(uint64_t a, uint64_t q) { return a ? q - a : 0; }
+
+}  // namespace nntt

@@ -1,0 +1,431 @@
+// Negacyclic NTT / inverse NTT kernels for gfx950.
+//
+// Transform (the library's contract; the pages leave the formula open):
+//   forward: ahat[k] = sum_i a[i] psi^((2 brv(k) + 1) i) mod q  (bit-reversed slots)
+//   inverse: a[i] = n^-1 sum_k ahat[k] psi^(-(2 brv(k) + 1) i)
+// computed in place by the decimation-in-time (Cooley-Tukey) network with the
+// psi^brv table, and by the decimation-in-frequency (Gentleman-Sande) network
+// with the psi^-brv table.
+//
+// Stage numbering.  In a transform of size M = 2^m, stage sigma (0 <= sigma < m)
+// has 2^sigma butterfly groups at distance M / 2^(sigma+1); the butterfly at
+// position j uses table[prefix * 2^sigma + j / (2 * distance)].  A transform of
+// size N split into N1 x N2 (row-major, N2 contiguous) runs stages 0..log N1-1
+// as N2 independent column transforms (prefix 1) and the remaining stages as N1
+// row transforms, row r with prefix N1 + r (the subtree of the bit-reversed
+// table rooted at N1 + r).  The same indexing serves both directions; the
+// forward network walks sigma upwards, the inverse downwards.
+//
+// Kernels:
+//   ntt_lds_kernel  : whole limb resident in LDS, n <= 2^14 (128 KiB of
+//                     residues fit the 160 KiB LDS of one gfx950 workgroup).
+//   ntt_col_kernel / ntt_row_kernel : the two halves for n = 2^15, 2^16; the
+//                     intermediate goes through L2/MALL/HBM between launches.
+// Inside a workgroup, each thread holds one radix-2^r "set" (up to 16 residues)
+// in registers and runs r stages on it; sets are exchanged through LDS between
+// passes.  LDS rows are padded by one slot per 128 bytes so strided set accesses
+// spread over the banks.
+#include "internal.h"
+
+namespace nntt {
+namespace {
+
+// Split m stages into passes of at most 4 (radix 16), as even as possible.
+struct Sched {
+  int np;
+  int r[5];
+  int s[5];
+};
+constexpr Sched make_sched(int logm) {
+  Sched S{};
+  S.np = logm <= 4 ? 1 : (logm + 3) / 4;
+  int base = logm / S.np, extra = logm % S.np, s = 0;
+  for (int i = 0; i < S.np; ++i) {
+    S.r[i] = base + (i < extra ? 1 : 0);
+    S.s[i] = s;
+    s += S.r[i];
+  }
+  return S;
+}
+
+template <class A>
+constexpr int sub_stride(int m) {
+  return (1 << m) + ((1 << m) >> A::kPadShift) + 1;
+}
+
+template <class A>
+__device__ __forceinline__ int lpos(int pos) {
+  return pos + (pos >> A::kPadShift);
+}
+
+// Per-sub-transform parameters seen by the pass executor.
+template <class A>
+struct SubParams {
+  const typename A::Tw* tw;  // this prime's table (n entries)
+  typename A::T q;
+  uint32_t prefix;
+};
+
+// One pass: radix 2^R sets over stages [S0, S0 + R) of every sub-transform held
+// in LDS.  NSUB sub-transforms of size 2^LOGM, NT threads.
+template <class A, bool FWD, int LOGM, int R, int S0, int NSUB, int NT, class GetSub>
+__device__ __forceinline__ void run_pass(typename A::T* lds, int tid, const GetSub& get_sub) {
+  using T = typename A::T;
+  constexpr int M = 1 << LOGM;
+  constexpr int SETS_PER_SUB = M >> R;
+  constexpr int TP = M >> (S0 + R);  // smallest distance in this pass
+  constexpr int SPAN = M >> S0;      // extent of one group at stage S0
+  constexpr int SETS = NSUB * SETS_PER_SUB;
+  constexpr int STRIDE = sub_stride<A>(LOGM);
+  static_assert(SETS % NT == 0, "sets must divide evenly");
+#pragma unroll
+  for (int it = 0; it < SETS / NT; ++it) {
+    const int set = tid + it * NT;
+    const int sub = set / SETS_PER_SUB, u = set % SETS_PER_SUB;
+    const int g = u / TP, r = u % TP;
+    const int pos0 = g * SPAN + r;
+    T* base = lds + sub * STRIDE;
+    const SubParams<A> sp = get_sub(sub);
+    const T q = sp.q, two_q = q + q;
+    const uint32_t pg = (sp.prefix << S0) + (uint32_t)g;
+    T x[1 << R];
+#pragma unroll
+    for (int i = 0; i < (1 << R); ++i) x[i] = base[lpos<A>(pos0 + i * TP)];
+    if (FWD) {
+#pragma unroll
+      for (int v = 0; v < R; ++v) {
+        const int half = 1 << (R - 1 - v);
+#pragma unroll
+        for (int i = 0; i < (1 << R); ++i) {
+          if (i & half) continue;
+          const typename A::Tw w = sp.tw[(pg << v) + (uint32_t)(i >> (R - v))];
+          ct_butterfly<A>(x[i], x[i + half], w, q, two_q);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int v = R - 1; v >= 0; --v) {
+        const int half = 1 << (R - 1 - v);
+#pragma unroll
+        for (int i = 0; i < (1 << R); ++i) {
+          if (i & half) continue;
+          const typename A::Tw w = sp.tw[(pg << v) + (uint32_t)(i >> (R - v))];
+          gs_butterfly<A>(x[i], x[i + half], w, q, two_q);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < (1 << R); ++i) base[lpos<A>(pos0 + i * TP)] = x[i];
+  }
+}
+
+// All passes of a sub-transform of size 2^LOGM, forward (sigma up) or inverse
+// (sigma down).  Ends with a barrier.
+template <class A, bool FWD, int LOGM, int NSUB, int NT, int P, class GetSub>
+__device__ __forceinline__ void run_passes(typename A::T* lds, int tid, const GetSub& get_sub) {
+  constexpr Sched S = make_sched(LOGM);
+  if constexpr (P < S.np) {
+    constexpr int idx = FWD ? P : S.np - 1 - P;
+    run_pass<A, FWD, LOGM, S.r[idx], S.s[idx], NSUB, NT>(lds, tid, get_sub);
+    __syncthreads();
+    run_passes<A, FWD, LOGM, NSUB, NT, P + 1>(lds, tid, get_sub);
+  }
+}
+
+template <class A>
+__device__ __forceinline__ const typename A::Tw* table_of(const void* tw_all, uint32_t limb, uint32_t n) {
+  return reinterpret_cast<const typename A::Tw*>(tw_all) + (size_t)limb * n;
+}
+
+template <class A>
+__device__ __forceinline__ typename A::T modulus(const ModInfo& m) {
+  return (typename A::T)m.q;
+}
+
+// Final store conversion: forward [0, 4q) -> [0, q); inverse: * n^-1 then [0, q).
+template <class A, bool FWD>
+__device__ __forceinline__ uint64_t finish(typename A::T x, const ModInfo& m) {
+  using T = typename A::T;
+  const T q = (T)m.q;
+  if (FWD) {
+    x = csub<T>(x, q + q);
+    return A::widen(csub<T>(x, q));
+  }
+  typename A::Tw s;
+  if constexpr (sizeof(T) == 8) {
+    s.w = m.n_inv;
+    s.wp = m.n_inv_shoup;
+  } else {
+    s.w = m.n_inv32;
+    s.wp = m.n_inv_shoup32;
+  }
+  return A::widen(csub<T>(A::mul(x, s, q), q));
+}
+
+// ---------------------------------------------------------------------------
+// Whole limb in LDS.
+template <int LOGN>
+struct LdsCfg {
+  static constexpr Sched S = make_sched(LOGN);
+  static constexpr int RMAX = S.r[0];
+  static constexpr int N = 1 << LOGN;
+  static constexpr int NT = (N >> RMAX) >= 256 ? (N >> RMAX) : 256;
+  static constexpr int ROWS = (NT << RMAX) / N;
+};
+
+template <class A, int LOGN, bool FWD>
+__global__ __launch_bounds__(LdsCfg<LOGN>::NT) void ntt_lds_kernel(uint64_t* __restrict__ data,
+                                                                   const void* __restrict__ tw_all,
+                                                                   const ModInfo* __restrict__ mods,
+                                                                   uint32_t num_limbs, uint32_t limb_begin,
+                                                                   uint64_t total_rows) {
+  using T = typename A::T;
+  using C = LdsCfg<LOGN>;
+  constexpr int N = C::N, ROWS = C::ROWS, NT = C::NT;
+  constexpr int STRIDE = sub_stride<A>(LOGN);
+  __shared__ T lds[ROWS * STRIDE];
+  const int tid = threadIdx.x;
+  const uint64_t row0 = (uint64_t)blockIdx.x * ROWS;
+
+  // Coalesced load, two residues per thread per step.
+  for (int e = 2 * tid; e < ROWS * N; e += 2 * NT) {
+    const int sub = e / N, pos = e % N;
+    if (row0 + sub < total_rows) {
+      const ulonglong2 v = *reinterpret_cast<const ulonglong2*>(data + (row0 + sub) * N + pos);
+      lds[sub * STRIDE + lpos<A>(pos)] = (T)v.x;
+      lds[sub * STRIDE + lpos<A>(pos + 1)] = (T)v.y;
+    }
+  }
+  __syncthreads();
+
+  auto get_sub = [&](int sub) {
+    const uint32_t limb = limb_begin + (uint32_t)((row0 + sub) % num_limbs);
+    SubParams<A> sp;
+    sp.tw = table_of<A>(tw_all, limb, N);
+    sp.q = modulus<A>(mods[limb]);
+    sp.prefix = 1;
+    return sp;
+  };
+  run_passes<A, FWD, LOGN, ROWS, NT, 0>(lds, tid, get_sub);
+
+  for (int e = 2 * tid; e < ROWS * N; e += 2 * NT) {
+    const int sub = e / N, pos = e % N;
+    if (row0 + sub < total_rows) {
+      const ModInfo& m = mods[limb_begin + (uint32_t)((row0 + sub) % num_limbs)];
+      ulonglong2 v;
+      v.x = finish<A, FWD>(lds[sub * STRIDE + lpos<A>(pos)], m);
+      v.y = finish<A, FWD>(lds[sub * STRIDE + lpos<A>(pos + 1)], m);
+      *reinterpret_cast<ulonglong2*>(data + (row0 + sub) * N + pos) = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Two-pass split for n = N1 * N2 (N2 contiguous).  Column kernel: a workgroup
+// owns COLS adjacent columns (COLS * 8 B = one 128 B line per row) of one limb.
+// Row kernel: a workgroup owns ROWS consecutive rows of one limb.
+constexpr int kCols = 16;
+constexpr int kRows = 16;
+
+template <int LOGN1>
+struct ColCfg {
+  static constexpr Sched S = make_sched(LOGN1);
+  static constexpr int NT = (kCols << LOGN1) >> S.r[0];
+};
+template <int LOGN2>
+struct RowCfg {
+  static constexpr Sched S = make_sched(LOGN2);
+  static constexpr int NT = (kRows << LOGN2) >> S.r[0];
+};
+
+// LAST: this launch finishes the transform (canonical output; inverse scaling).
+template <class A, int LOGN1, int LOGN2, bool FWD, bool LAST>
+__global__ __launch_bounds__(ColCfg<LOGN1>::NT) void ntt_col_kernel(uint64_t* __restrict__ data,
+                                                                    const void* __restrict__ tw_all,
+                                                                    const ModInfo* __restrict__ mods,
+                                                                    uint32_t num_limbs, uint32_t limb_begin) {
+  using T = typename A::T;
+  constexpr int N1 = 1 << LOGN1, N2 = 1 << LOGN2, N = N1 * N2;
+  constexpr int NT = ColCfg<LOGN1>::NT;
+  constexpr int STRIDE = sub_stride<A>(LOGN1);
+  constexpr int BLOCKS_PER_LIMB = N2 / kCols;
+  __shared__ T lds[kCols * STRIDE];
+  const int tid = threadIdx.x;
+  const uint64_t row = blockIdx.x / BLOCKS_PER_LIMB;
+  const int c0 = (blockIdx.x % BLOCKS_PER_LIMB) * kCols;
+  const uint32_t limb = limb_begin + (uint32_t)(row % num_limbs);
+  uint64_t* base = data + row * N + c0;
+
+  for (int e = 2 * tid; e < kCols * N1; e += 2 * NT) {
+    const int rr = e / kCols, c = e % kCols;
+    const ulonglong2 v = *reinterpret_cast<const ulonglong2*>(base + (size_t)rr * N2 + c);
+    lds[c * STRIDE + lpos<A>(rr)] = (T)v.x;
+    lds[(c + 1) * STRIDE + lpos<A>(rr)] = (T)v.y;
+  }
+  __syncthreads();
+
+  const ModInfo& m = mods[limb];
+  SubParams<A> sp;
+  sp.tw = table_of<A>(tw_all, limb, N);
+  sp.q = modulus<A>(m);
+  sp.prefix = 1;
+  auto get_sub = [&](int) { return sp; };
+  run_passes<A, FWD, LOGN1, kCols, NT, 0>(lds, tid, get_sub);
+
+  for (int e = 2 * tid; e < kCols * N1; e += 2 * NT) {
+    const int rr = e / kCols, c = e % kCols;
+    ulonglong2 v;
+    if (LAST) {
+      v.x = finish<A, FWD>(lds[c * STRIDE + lpos<A>(rr)], m);
+      v.y = finish<A, FWD>(lds[(c + 1) * STRIDE + lpos<A>(rr)], m);
+    } else {
+      v.x = A::widen(lds[c * STRIDE + lpos<A>(rr)]);
+      v.y = A::widen(lds[(c + 1) * STRIDE + lpos<A>(rr)]);
+    }
+    *reinterpret_cast<ulonglong2*>(base + (size_t)rr * N2 + c) = v;
+  }
+}
+
+template <class A, int LOGN1, int LOGN2, bool FWD, bool LAST>
+__global__ __launch_bounds__(RowCfg<LOGN2>::NT) void ntt_row_kernel(uint64_t* __restrict__ data,
+                                                                    const void* __restrict__ tw_all,
+                                                                    const ModInfo* __restrict__ mods,
+                                                                    uint32_t num_limbs, uint32_t limb_begin) {
+  using T = typename A::T;
+  constexpr int N1 = 1 << LOGN1, N2 = 1 << LOGN2, N = N1 * N2;
+  constexpr int NT = RowCfg<LOGN2>::NT;
+  constexpr int STRIDE = sub_stride<A>(LOGN2);
+  constexpr int BLOCKS_PER_LIMB = N1 / kRows;
+  __shared__ T lds[kRows * STRIDE];
+  const int tid = threadIdx.x;
+  const uint64_t row = blockIdx.x / BLOCKS_PER_LIMB;
+  const int r0 = (blockIdx.x % BLOCKS_PER_LIMB) * kRows;
+  const uint32_t limb = limb_begin + (uint32_t)(row % num_limbs);
+  uint64_t* base = data + row * N + (size_t)r0 * N2;
+
+  for (int e = 2 * tid; e < kRows * N2; e += 2 * NT) {
+    const int sub = e / N2, pos = e % N2;
+    const ulonglong2 v = *reinterpret_cast<const ulonglong2*>(base + e);
+    lds[sub * STRIDE + lpos<A>(pos)] = (T)v.x;
+    lds[sub * STRIDE + lpos<A>(pos + 1)] = (T)v.y;
+  }
+  __syncthreads();
+
+  const ModInfo& m = mods[limb];
+  const typename A::Tw* tw = table_of<A>(tw_all, limb, N);
+  const T q = modulus<A>(m);
+  auto get_sub = [&](int sub) {
+    SubParams<A> sp;
+    sp.tw = tw;
+    sp.q = q;
+    sp.prefix = (uint32_t)(N1 + r0 + sub);
+    return sp;
+  };
+  run_passes<A, FWD, LOGN2, kRows, NT, 0>(lds, tid, get_sub);
+
+  for (int e = 2 * tid; e < kRows * N2; e += 2 * NT) {
+    const int sub = e / N2, pos = e % N2;
+    ulonglong2 v;
+    if (LAST) {
+      v.x = finish<A, FWD>(lds[sub * STRIDE + lpos<A>(pos)], m);
+      v.y = finish<A, FWD>(lds[sub * STRIDE + lpos<A>(pos + 1)], m);
+    } else {
+      v.x = A::widen(lds[sub * STRIDE + lpos<A>(pos)]);
+      v.y = A::widen(lds[sub * STRIDE + lpos<A>(pos + 1)]);
+    }
+    *reinterpret_cast<ulonglong2*>(base + e) = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <class A, int LOGN>
+hipError_t launch_lds(const ntt_plan* p, uint64_t* data, uint64_t rows, uint32_t limb_begin, uint32_t num_limbs,
+                      bool inverse, hipStream_t s) {
+  using C = LdsCfg<LOGN>;
+  const void* tw = sizeof(typename A::T) == 8 ? (inverse ? (const void*)p->d_inv : (const void*)p->d_fwd)
+                                              : (inverse ? (const void*)p->d_inv32 : (const void*)p->d_fwd32);
+  const uint64_t blocks = (rows + C::ROWS - 1) / C::ROWS;
+  if (inverse)
+    hipLaunchKernelGGL((ntt_lds_kernel<A, LOGN, false>), dim3((uint32_t)blocks), dim3(C::NT), 0, s, data, tw,
+                       p->d_mods, num_limbs, limb_begin, rows);
+  else
+    hipLaunchKernelGGL((ntt_lds_kernel<A, LOGN, true>), dim3((uint32_t)blocks), dim3(C::NT), 0, s, data, tw,
+                       p->d_mods, num_limbs, limb_begin, rows);
+  return hipGetLastError();
+}
+
+template <class A, int LOGN1, int LOGN2>
+hipError_t launch_split(const ntt_plan* p, uint64_t* data, uint64_t rows, uint32_t limb_begin, uint32_t num_limbs,
+                        bool inverse, hipStream_t s) {
+  const void* tw = sizeof(typename A::T) == 8 ? (inverse ? (const void*)p->d_inv : (const void*)p->d_fwd)
+                                              : (inverse ? (const void*)p->d_inv32 : (const void*)p->d_fwd32);
+  const uint32_t col_blocks = (uint32_t)(rows * ((1u << LOGN2) / kCols));
+  const uint32_t row_blocks = (uint32_t)(rows * ((1u << LOGN1) / kRows));
+  if (!inverse) {
+    hipLaunchKernelGGL((ntt_col_kernel<A, LOGN1, LOGN2, true, false>), dim3(col_blocks), dim3(ColCfg<LOGN1>::NT), 0,
+                       s, data, tw, p->d_mods, num_limbs, limb_begin);
+    hipLaunchKernelGGL((ntt_row_kernel<A, LOGN1, LOGN2, true, true>), dim3(row_blocks), dim3(RowCfg<LOGN2>::NT), 0,
+                       s, data, tw, p->d_mods, num_limbs, limb_begin);
+  } else {
+    hipLaunchKernelGGL((ntt_row_kernel<A, LOGN1, LOGN2, false, false>), dim3(row_blocks), dim3(RowCfg<LOGN2>::NT),
+                       0, s, data, tw, p->d_mods, num_limbs, limb_begin);
+    hipLaunchKernelGGL((ntt_col_kernel<A, LOGN1, LOGN2, false, true>), dim3(col_blocks), dim3(ColCfg<LOGN1>::NT), 0,
+                       s, data, tw, p->d_mods, num_limbs, limb_begin);
+  }
+  return hipGetLastError();
+}
+
+template <class A>
+hipError_t launch_any(const ntt_plan* p, uint64_t* data, uint64_t rows, uint32_t limb_begin, uint32_t num_limbs,
+                      bool inverse, hipStream_t s) {
+  switch (p->logn) {
+#define NNTT_CASE(L) \
+  case L:            \
+    return launch_lds<A, L>(p, data, rows, limb_begin, num_limbs, inverse, s);
+    NNTT_CASE(1)
+    NNTT_CASE(2)
+    NNTT_CASE(3)
+    NNTT_CASE(4)
+    NNTT_CASE(5)
+    NNTT_CASE(6)
+    NNTT_CASE(7)
+    NNTT_CASE(8)
+    NNTT_CASE(9)
+    NNTT_CASE(10)
+    NNTT_CASE(11)
+    NNTT_CASE(12)
+    NNTT_CASE(13)
+    NNTT_CASE(14)
+#undef NNTT_CASE
+    case 15:
+      return launch_split<A, 7, 8>(p, data, rows, limb_begin, num_limbs, inverse, s);
+    case 16:
+      return launch_split<A, 8, 8>(p, data, rows, limb_begin, num_limbs, inverse, s);
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+bool range_is_narrow(const ntt_plan* p, uint32_t limb_begin, uint32_t num_limbs) {
+  for (uint32_t l = limb_begin; l < limb_begin + num_limbs; ++l)
+    if (!p->narrow[l]) return false;
+  return true;
+}
+
+hipError_t launch_ntt(const ntt_plan* p, uint64_t* data, uint64_t batch, uint32_t limb_begin, uint32_t num_limbs,
+                      bool inverse, hipStream_t s) {
+  const uint64_t rows = batch * num_limbs;
+  if (rows == 0) return hipSuccess;
+  if (range_is_narrow(p, limb_begin, num_limbs))
+    return launch_any<Narrow>(p, data, rows, limb_begin, num_limbs, inverse, s);
+  return launch_any<Wide>(p, data, rows, limb_begin, num_limbs, inverse, s);
+}
+
+hipError_t launch_ntt_galois(const ntt_plan*, uint64_t*, const uint64_t*, uint64_t, uint64_t, uint32_t, uint32_t,
+                             hipStream_t) {
+  return hipErrorNotSupported;
+}
+
+}  // namespace nntt
