@@ -1,0 +1,223 @@
+#!/usr/bin/env python3
+"""Throughput benchmark on one MI355X.
+
+One step = one pass of every hot-path operation over one batch of the
+large-ring workload (n = 2^16, 24 primes of 60 bits, 8 ciphertexts = 16
+polynomials, tensor [8][2][24][65536], seeded uniform residues):
+  1. forward NTT of A                                  (384 limb-NTTs)
+  2. pointwise product  C = A_hat * B_hat              (NTT domain)
+  3. ciphertext tensor product D = (A_hat, B_hat)      ([8][3][24][n])
+  4. inverse NTT of C                                  (384 limb-INTTs)
+  5. coefficient-domain automorphism E = sigma_g(C), g = 5^(2^(s mod 16)) mod 2n
+  6. one rotation key-switch of a 1-ciphertext batch (Q = 24, P = 8, dnum = 3)
+     with the same g (96 forward + 64 inverse limb transforms inside)
+`value` is limb-NTTs per second over whole steps (forward and inverse
+transforms, those inside the key-switch included).  Inputs are resident in HBM
+before timing; the timed steps rotate over enough distinct buffers and keys
+(> 1 GB) that the 256 MB Infinity Cache cannot hold them.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--rotate", type=int, default=3, help="distinct input sets cycled through")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-limbs", type=int, default=48,
+                    help="limbs of the batch the oracle processes for the CPU baseline")
+    return ap.parse_args()
+
+
+def cpu_baseline(primes, n, nq, npr, dnum, sample_limbs, a_host, b_host, ct_host, ksk_host, g):
+    """The plain-C oracle on a bounded sample of one step, timed on the host cores."""
+    import numpy as np
+
+    import oracle as orc
+    threads = orc.default_threads()
+    L = nq
+    rows = max(1, sample_limbs // L)  # whole polynomials of the batch
+    a = np.ascontiguousarray(a_host.reshape(-1, L, n)[:rows])
+    b = np.ascontiguousarray(b_host.reshape(-1, L, n)[:rows])
+    qs = primes[:L]
+    t0 = time.perf_counter()
+    ah = orc.batch_ntt(a, qs, threads=threads)
+    c = orc.batch_pointwise(ah, b, qs)
+    if rows % 2 == 0:
+        orc.batch_tensor(ah.reshape(-1, 2, L, n), b.reshape(-1, 2, L, n), qs)
+    c = orc.batch_ntt(c, qs, inverse=True, threads=threads)
+    orc.batch_automorph(c, g, 0, qs)
+    orc.keyswitch(ct_host, ksk_host, g, primes[: nq + npr], nq, dnum, threads=threads)
+    dt = time.perf_counter() - t0
+    limb_ntts = 2 * rows * L + dnum * (nq + npr) + 2 * (nq + npr)
+    return {
+        "value": limb_ntts / dt,
+        "unit": "limb-NTT/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{rows} of the 16 polynomials (forward NTT, pointwise, tensor, inverse NTT, automorphism) "
+                   f"plus one key-switch: {limb_ntts} limb transforms in {dt:.2f} s"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1", "n_gpus": args.gpus}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from negacyclic_ntt_amd import binding as B
+    from negacyclic_ntt_amd import inputs, workloads
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    W, KS = workloads.RING, workloads.KEYSWITCH
+    n, L, nq, npr, dnum = W.n, W.limbs, KS.limbs, KS.special, KS.dnum
+    primes = B.find_primes(W.bits, n, nq + npr)  # the ring's 24 primes are the first 24 of this list
+    plan = B.Plan(n, primes, 0)
+    galois = W.galois
+
+    # ---- inputs (host generation, then resident on the device) ----
+    t_gen = time.perf_counter()
+    a_host = inputs.uniform_residues(W.shape_a, primes[:L], W.seed_a)
+    b_host = inputs.uniform_residues(W.shape_a, primes[:L], W.seed_a + 1)
+    ct_host = inputs.uniform_residues(KS.shape_a, primes[:nq], KS.seed_a)
+    ksk_host = inputs.uniform_residues((dnum, 2, nq + npr, n), primes[: nq + npr], KS.seed_b)
+    a0, b0 = B.to_device(a_host), B.to_device(b_host)
+    sets = [(a0, b0)] + [(a0.clone(), b0.clone()) for _ in range(args.rotate - 1)]
+    ct = B.to_device(ct_host)
+    ksk0 = B.to_device(ksk_host)
+    keys = [ksk0] + [ksk0.clone() for _ in range(max(0, 2 * args.rotate - 1))]
+    C = torch.empty_like(a0)
+    E = torch.empty_like(a0)
+    D = torch.empty((W.shape_a[0], 3, L, n), dtype=torch.int64, device=dev)
+    ks_out = torch.empty_like(ct)
+    try:
+        ksp = B.KeySwitchPlan(plan, nq, npr, dnum)
+        ws = B.workspace(ksp, 1)
+    except B.NttError:
+        ksp = None
+    torch.cuda.synchronize()
+    gen_s = time.perf_counter() - t_gen
+    resident_bytes = sum(t.numel() * 8 for pair in sets for t in pair) + sum(k.numel() * 8 for k in keys)
+
+    rows = ["ntt_forward", "poly_mul_ntt", "ct_tensor_ntt", "ntt_inverse", "automorph", "keyswitch"]
+    ev = {r: [] for r in rows}
+
+    def step(s, timed):
+        a, b = sets[s % len(sets)]
+        g = galois[s % len(galois)]
+
+        def run(name, fn):
+            if timed:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                ev[name].append((e0, e1))
+            else:
+                fn()
+
+        run("ntt_forward", lambda: B.ntt_forward(plan, a))
+        run("poly_mul_ntt", lambda: B.poly_mul_ntt(plan, C, a, b))
+        run("ct_tensor_ntt", lambda: B.ct_tensor_ntt(plan, D, a, b))
+        run("ntt_inverse", lambda: B.ntt_inverse(plan, C))
+        run("automorph", lambda: B.automorph(plan, E, C, g, 0))
+        if ksp is not None:
+            run("keyswitch", lambda: B.keyswitch(ksp, ks_out, ct, keys[s % len(keys)], g, ws))
+
+    for s in range(args.warmup):
+        step(s, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(args.warmup + s, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms = {r: [e0.elapsed_time(e1) for e0, e1 in ev[r]] for r in rows if ev[r]}
+    mean_ms = {r: sum(v) / len(v) for r, v in ms.items()}
+    polys = W.shape_a[0] * W.shape_a[1]
+    limb = polys * L
+    ks_limb_ntts = (dnum * (nq + npr) + 2 * (nq + npr)) if ksp is not None else 0
+    limb_ntts_per_step = 2 * limb + ks_limb_ntts
+    ms_per_step = wall * 1e3 / args.steps
+    value = limb_ntts_per_step / (ms_per_step * 1e-3)
+
+    # algorithmic bytes per call (each residue read and written once; 8 B each)
+    elem = limb * n
+    alg_bytes = {
+        "ntt_forward": 16 * elem,
+        "ntt_inverse": 16 * elem,
+        "poly_mul_ntt": 24 * elem,
+        "ct_tensor_ntt": 56 * elem // 2,
+        "automorph": 16 * elem,
+        "keyswitch": 8 * n * (2 * nq + dnum * 2 * (nq + npr) + 2 * nq),
+    }
+    per_row = {}
+    for r, m in mean_ms.items():
+        gbps = alg_bytes[r] / (m * 1e-3) / 1e9
+        per_row[r] = {"ms": round(m, 4), "alg_GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
+    per_row["ntt_forward"]["limb_ntt_per_s"] = round(limb / (mean_ms["ntt_forward"] * 1e-3))
+    per_row["ntt_inverse"]["limb_ntt_per_s"] = round(limb / (mean_ms["ntt_inverse"] * 1e-3))
+    if "keyswitch" in mean_ms:
+        per_row["keyswitch"]["keyswitch_per_s"] = round(1e3 / mean_ms["keyswitch"], 1)
+
+    dom = max(mean_ms, key=mean_ms.get)
+    dom_gbps = alg_bytes[dom] / (mean_ms[dom] * 1e-3) / 1e9
+    roofline = {
+        "kernel": dom,
+        "bound": "hbm",
+        "achieved": round(dom_gbps, 1),
+        "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
+        "traffic": None,
+    }
+    rt_ms = mean_ms["ntt_forward"] + mean_ms["ntt_inverse"]
+    out = {
+        "metric": "limb-NTTs/sec + achieved HBM GB/s (N=2^16, 60-bit, 1 GPU); keyswitches/sec",
+        "value": round(value, 1),
+        "unit": "limb-NTT/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u64",
+        "data": "synthetic",
+        "config": {"workload": W.name, "n": n, "primes": f"{L} x 60-bit", "batch": list(W.shape_a),
+                   "keyswitch": KS.name, "rotated_sets": len(sets), "resident_GB": round(resident_bytes / 1e9, 2)},
+        "ntt_round_trip": {"limb_ntt_per_s": round(2 * limb / (rt_ms * 1e-3)),
+                           "alg_GBps": round(32 * elem / (rt_ms * 1e-3) / 1e9, 1)},
+        "keyswitches_per_s": per_row.get("keyswitch", {}).get("keyswitch_per_s"),
+        "rows": per_row,
+        "roofline": roofline,
+        "input_gen_s": round(gen_s, 2),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(primes, n, nq, npr, dnum, args.cpu_sample_limbs, a_host, b_host,
+                                           ct_host, ksk_host, galois[0])
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,17 +1,399 @@
-// Rotation key-switch (placeholder until the kernels land).
+// Hybrid rotation key-switch on gfx950.
+//
+// For a ciphertext (c0, c1) over Q = q_0..q_{L-1}, special primes P = p_0..p_{K-1}
+// and dnum digits of alpha = L / dnum consecutive primes:
+//   1. c' = sigma_g(c): the automorphism X -> X^g (coefficient domain), gathered
+//      on load inside steps 2 and 6 (no separate pass over memory);
+//   2. ModUp: digit j of c1' is lifted to the unique integer D_j in [0, Q_j)
+//      (Garner / mixed radix -- the "mixed-radix decomposition and basis
+//      extension" of FHElium "Eager, Compile, and native execution", section
+//      "CUDA execution"; the "Garner extension" of the kestrel-llm overview,
+//      section 4.2) and reduced onto every prime of Q u P;
+//   3. forward NTT of every extended digit;
+//   4. key inner product acc_c = sum_j NTT(D_j) * ksk[j][c] (FHElium's key-switch
+//      multiply-accumulate);
+//   5. inverse NTT of both accumulators;
+//   6. ModDown (exact floor, FHElium's "QP-to-Q ModDown"):
+//      out_c = floor(X_c / P) mod q_l = (acc_c[l] - (X_c mod P)) * P^-1 mod q_l,
+//      X_c mod P from the P residues by Garner; out_0 += sigma_g(c0).
+// Garner: with residues x_i modulo m_i, the mixed-radix digits are
+//   v_i = (x_i - sum_{k<i} v_k prod_{j<k} m_j) * (prod_{j<i} m_j)^-1  mod m_i,
+// and D = sum_i v_i prod_{j<i} m_j lies in [0, prod m_i); D mod p is then
+// sum_i v_i (prod_{j<i} m_j mod p).  Every product is a Shoup product by a
+// plan constant; partial sums stay in [0, 2p).
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+
 #include "internal.h"
 
-struct ntt_ks_plan {
-  int unused;
+namespace nntt {
+namespace {
+
+constexpr int kKsThreads = 256;
+constexpr int kMaxDigitPrimes = 16;  // table row strides of the device constants
+constexpr int kMaxSpecial = 16;
+
+using Tw = Wide::Tw;
+
+__device__ __forceinline__ uint64_t shoup(uint64_t y, Tw c, uint64_t q) { return Wide::mul(y, c, q); }
+
+// acc, t in [0, 2q) -> (acc + t) in [0, 2q)
+__device__ __forceinline__ uint64_t lazy_add(uint64_t acc, uint64_t t, uint64_t two_q) {
+  return csub(acc + t, two_q);
+}
+
+// Garner digits of k residues (k <= K, runtime).  m[i] the moduli, g[i * S + k]
+// (S = table row stride) holds prod_{j<k} m_j mod m_i for k < i and
+// (prod_{j<i} m_j)^-1 mod m_i at k = i.  Output v[i] canonical mod m[i].
+template <int K, int S>
+__device__ __forceinline__ void garner(const uint64_t (&x)[K], uint64_t (&v)[K], uint32_t k,
+                                       const uint64_t* __restrict__ m, const Tw* __restrict__ g) {
+  static_assert(K <= S, "register width exceeds the table stride");
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    if (i >= (int)k) break;
+    const uint64_t mi = m[i], two = mi + mi;
+    uint64_t s = 0;
+#pragma unroll
+    for (int kk = 0; kk < i; ++kk) s = lazy_add(s, shoup(v[kk], g[i * S + kk], mi), two);
+    // x_i - s + 2 m_i in (0, 3 m_i)
+    const uint64_t y = x[i] + two - s;
+    v[i] = csub(i == 0 ? x[0] : shoup(y, g[i * S + i], mi), mi);
+  }
+}
+
+// sum_i v_i c_i mod p, canonical.  c[i] = prod_{j<i} m_j mod p (Shoup pairs).
+template <int K>
+__device__ __forceinline__ uint64_t mixed_radix_eval(const uint64_t (&v)[K], uint32_t k, const Tw* __restrict__ c,
+                                                     uint64_t p) {
+  const uint64_t two = p + p;
+  uint64_t s = 0;
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    if (i >= (int)k) break;
+    s = lazy_add(s, shoup(v[i], c[i], p), two);
+  }
+  return csub(s, p);
+}
+
+// Coefficient-domain automorphism gather: value of sigma_g(a) at position e.
+// i = e * h mod 2n with h = g^-1 mod 2n; sigma_g(a)[e] = a[i] (i < n) or -a[i - n].
+struct Gather {
+  uint32_t src;
+  bool neg;
+};
+__device__ __forceinline__ Gather gather_index(uint32_t e, uint32_t h, uint32_t logn) {
+  const uint32_t n = 1u << logn;
+  const uint32_t i = (uint32_t)(((uint64_t)e * h) & (2 * n - 1));
+  return Gather{i & (n - 1), i >= n};
+}
+
+// Device constants of a key-switch plan (one allocation, offsets in elements).
+struct KsDev {
+  const uint64_t* moduli;   // [nq + np]
+  const Tw* digit_garner;   // [dnum][K][K]   (K = kMaxDigitPrimes)
+  const Tw* digit_eval;     // [dnum][nq+np][K]
+  const Tw* p_garner;       // [KP][KP]       (KP = kMaxSpecial)
+  const Tw* p_eval;         // [nq][KP]
+  const Tw* p_inv;          // [nq]
 };
 
-extern "C" int keyswitch_plan_create(ntt_ks_plan** out, const ntt_plan*, uint32_t, uint32_t, uint32_t) {
-  if (out) *out = nullptr;
-  return NTT_EUNSUPPORTED;
+// ---- ModUp with the automorphism fused on load ---------------------------------
+// grid.x: coefficient tiles; grid.y: batch * dnum.  ext: [batch][dnum][nq+np][n].
+template <int K>
+__global__ __launch_bounds__(kKsThreads) void modup_kernel(uint64_t* __restrict__ ext,
+                                                           const uint64_t* __restrict__ ct, KsDev kc, uint32_t logn,
+                                                           uint32_t h, uint32_t nq, uint32_t np_, uint32_t alpha,
+                                                           uint32_t dnum) {
+  const uint32_t n = 1u << logn;
+  const uint32_t e = blockIdx.x * kKsThreads + threadIdx.x;
+  if (e >= n) return;
+  const uint32_t bj = blockIdx.y, b = bj / dnum, j = bj % dnum;
+  const uint32_t nqp = nq + np_;
+  const uint64_t* c1 = ct + ((uint64_t)b * 2 + 1) * nq * n;
+  const Gather gi = gather_index(e, h, logn);
+  const uint32_t first = j * alpha;
+  uint64_t x[K], v[K];
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    if (i >= (int)alpha) break;
+    const uint64_t q = kc.moduli[first + i];
+    const uint64_t a = c1[(uint64_t)(first + i) * n + gi.src];
+    x[i] = gi.neg ? neg_mod(a, q) : a;
+  }
+  uint64_t* out = ext + (uint64_t)bj * nqp * n + e;
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    if (i >= (int)alpha) break;
+    out[(uint64_t)(first + i) * n] = x[i];  // the digit's own primes keep their residues
+  }
+  constexpr int S = kMaxDigitPrimes;
+  garner<K, S>(x, v, alpha, kc.moduli + first, kc.digit_garner + (size_t)j * S * S);
+  const Tw* ev = kc.digit_eval + (size_t)j * nqp * S;
+  for (uint32_t t = 0; t < nqp; ++t) {
+    if (t >= first && t < first + alpha) continue;
+    out[(uint64_t)t * n] = mixed_radix_eval<K>(v, alpha, ev + (size_t)t * S, kc.moduli[t]);
+  }
 }
-extern "C" int keyswitch_workspace_size(const ntt_ks_plan*, uint64_t, size_t*) { return NTT_EUNSUPPORTED; }
-extern "C" int keyswitch(const ntt_ks_plan*, uint64_t*, const uint64_t*, const uint64_t*, uint64_t, uint64_t, void*,
-                         size_t, void*) {
-  return NTT_EUNSUPPORTED;
+
+// ---- key inner product -----------------------------------------------------------
+// acc[b][c][t][e] = sum_j ext[b][j][t][e] * ksk[j][c][t][e]  (mod q_t), two coefficients per thread.
+__global__ __launch_bounds__(kKsThreads) void mac_kernel(uint64_t* __restrict__ acc, const uint64_t* __restrict__ ext,
+                                                         const uint64_t* __restrict__ ksk,
+                                                         const ModInfo* __restrict__ mods, uint32_t logn,
+                                                         uint32_t nqp, uint32_t dnum, uint64_t pairs_per_batch) {
+  const uint64_t p = (uint64_t)blockIdx.x * kKsThreads + threadIdx.x;
+  const uint32_t b = blockIdx.y;
+  if (p >= pairs_per_batch) return;
+  const uint64_t off = 2 * p;  // index in [nqp][n]
+  const uint32_t t = (uint32_t)(off >> logn);
+  const Barrett br = mods[t].br;
+  const uint64_t q = br.q;
+  const uint64_t plane = (uint64_t)nqp << logn;
+  const uint64_t* xe = ext + (uint64_t)b * dnum * plane + off;
+  ulonglong2 s0 = {0, 0}, s1 = {0, 0};
+  for (uint32_t j = 0; j < dnum; ++j) {
+    const ulonglong2 d = *reinterpret_cast<const ulonglong2*>(xe + (uint64_t)j * plane);
+    const ulonglong2 k0 = *reinterpret_cast<const ulonglong2*>(ksk + ((uint64_t)j * 2) * plane + off);
+    const ulonglong2 k1 = *reinterpret_cast<const ulonglong2*>(ksk + ((uint64_t)j * 2 + 1) * plane + off);
+    s0.x = add_mod(s0.x, barrett_mul(d.x, k0.x, br), q);
+    s0.y = add_mod(s0.y, barrett_mul(d.y, k0.y, br), q);
+    s1.x = add_mod(s1.x, barrett_mul(d.x, k1.x, br), q);
+    s1.y = add_mod(s1.y, barrett_mul(d.y, k1.y, br), q);
+  }
+  uint64_t* o = acc + (uint64_t)b * 2 * plane + off;
+  *reinterpret_cast<ulonglong2*>(o) = s0;
+  *reinterpret_cast<ulonglong2*>(o + plane) = s1;
 }
-extern "C" void keyswitch_plan_destroy(ntt_ks_plan*) {}
+
+// ---- ModDown + sigma_g(c0) ---------------------------------------------------------
+// grid.x: coefficient tiles; grid.y: batch * 2 (component).  acc: [batch][2][nq+np][n].
+template <int KP>
+__global__ __launch_bounds__(kKsThreads) void moddown_kernel(uint64_t* __restrict__ out,
+                                                             const uint64_t* __restrict__ acc,
+                                                             const uint64_t* __restrict__ ct, KsDev kc, uint32_t logn,
+                                                             uint32_t h, uint32_t nq, uint32_t np_) {
+  const uint32_t n = 1u << logn;
+  const uint32_t e = blockIdx.x * kKsThreads + threadIdx.x;
+  if (e >= n) return;
+  const uint32_t bc = blockIdx.y, b = bc >> 1, comp = bc & 1;
+  const uint32_t nqp = nq + np_;
+  const uint64_t* a = acc + (uint64_t)bc * nqp * n + e;
+  uint64_t y[KP], v[KP];
+#pragma unroll
+  for (int i = 0; i < KP; ++i) {
+    if (i >= (int)np_) break;
+    y[i] = a[(uint64_t)(nq + i) * n];
+  }
+  constexpr int S = kMaxSpecial;
+  garner<KP, S>(y, v, np_, kc.moduli + nq, kc.p_garner);
+  const uint64_t* c0 = ct + (uint64_t)b * 2 * nq * n;
+  const Gather gi = gather_index(e, h, logn);
+  uint64_t* o = out + (uint64_t)bc * nq * n + e;
+  for (uint32_t l = 0; l < nq; ++l) {
+    const uint64_t q = kc.moduli[l];
+    const uint64_t r = mixed_radix_eval<KP>(v, np_, kc.p_eval + (size_t)l * S, q);  // (X mod P) mod q_l
+    const uint64_t d = sub_mod(a[(uint64_t)l * n], r, q);
+    uint64_t res = csub(shoup(d, kc.p_inv[l], q), q);
+    if (comp == 0) {
+      const uint64_t s = c0[(uint64_t)l * n + gi.src];
+      res = add_mod(res, gi.neg ? neg_mod(s, q) : s, q);
+    }
+    o[(uint64_t)l * n] = res;
+  }
+}
+
+}  // namespace
+}  // namespace nntt
+
+using namespace nntt;
+
+struct ntt_ks_plan {
+  const ntt_plan* qp = nullptr;
+  uint32_t nq = 0, np = 0, dnum = 0, alpha = 0;
+  void* d_const = nullptr;
+  KsDev dev{};
+};
+
+namespace {
+
+Tw shoup_pair(uint64_t w, uint64_t q) {
+  return Tw{w, (uint64_t)(((unsigned __int128)w << 64) / q)};
+}
+
+// g[i * K + k]: prod_{j<k} m_j mod m_i (k < i), and (prod_{j<i} m_j)^-1 mod m_i (k == i).
+void garner_table(const uint64_t* m, uint32_t k, uint32_t K, Tw* g) {
+  for (uint32_t i = 0; i < k; ++i) {
+    uint64_t prod = 1 % m[i];
+    for (uint32_t kk = 0; kk < i; ++kk) {
+      g[i * K + kk] = shoup_pair(prod, m[i]);
+      prod = host_mulmod(prod, m[kk] % m[i], m[i]);
+    }
+    g[i * K + i] = shoup_pair(i ? host_invmod(prod, m[i]) : 1 % m[i], m[i]);
+  }
+}
+
+// c[i] = prod_{j<i} m_j mod p
+void eval_table(const uint64_t* m, uint32_t k, uint64_t p, Tw* c) {
+  uint64_t prod = 1 % p;
+  for (uint32_t i = 0; i < k; ++i) {
+    c[i] = shoup_pair(prod, p);
+    prod = host_mulmod(prod, m[i] % p, p);
+  }
+}
+
+}  // namespace
+
+extern "C" int keyswitch_plan_create(ntt_ks_plan** out, const ntt_plan* qp, uint32_t nq, uint32_t np_,
+                                     uint32_t dnum) {
+  if (!out) return NTT_EINVAL;
+  *out = nullptr;
+  if (!qp) return NTT_EINVAL;
+  if (qp->device < 0) return NTT_EDEVICE;
+  if (nq == 0 || np_ == 0 || dnum == 0 || nq % dnum != 0 || nq + np_ > qp->num_primes) return NTT_EINVAL;
+  const uint32_t alpha = nq / dnum;
+  if (alpha > (uint32_t)kMaxDigitPrimes || np_ > (uint32_t)kMaxSpecial) return NTT_EUNSUPPORTED;
+  const uint32_t nqp = nq + np_, K = (uint32_t)kMaxDigitPrimes, KP = (uint32_t)kMaxSpecial;
+  const uint64_t* m = qp->primes.data();
+
+  std::vector<uint64_t> moduli(m, m + nqp);
+  std::vector<Tw> dg((size_t)dnum * K * K, Tw{0, 0}), de((size_t)dnum * nqp * K, Tw{0, 0});
+  std::vector<Tw> pg((size_t)KP * KP, Tw{0, 0}), pe((size_t)nq * KP, Tw{0, 0}), pinv(nq);
+  for (uint32_t j = 0; j < dnum; ++j) {
+    garner_table(m + j * alpha, alpha, K, dg.data() + (size_t)j * K * K);
+    for (uint32_t t = 0; t < nqp; ++t) eval_table(m + j * alpha, alpha, m[t], de.data() + ((size_t)j * nqp + t) * K);
+  }
+  garner_table(m + nq, np_, KP, pg.data());
+  for (uint32_t l = 0; l < nq; ++l) {
+    eval_table(m + nq, np_, m[l], pe.data() + (size_t)l * KP);
+    uint64_t P = 1;
+    for (uint32_t i = 0; i < np_; ++i) P = host_mulmod(P, m[nq + i] % m[l], m[l]);
+    pinv[l] = shoup_pair(host_invmod(P, m[l]), m[l]);
+  }
+
+  const size_t sz_m = moduli.size() * 8, sz_dg = dg.size() * sizeof(Tw), sz_de = de.size() * sizeof(Tw);
+  const size_t sz_pg = pg.size() * sizeof(Tw), sz_pe = pe.size() * sizeof(Tw), sz_pi = pinv.size() * sizeof(Tw);
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t total = al(sz_m) + al(sz_dg) + al(sz_de) + al(sz_pg) + al(sz_pe) + al(sz_pi);
+  std::vector<uint8_t> blob(total, 0);
+  size_t off[6], o = 0;
+  const void* src[6] = {moduli.data(), dg.data(), de.data(), pg.data(), pe.data(), pinv.data()};
+  const size_t sz[6] = {sz_m, sz_dg, sz_de, sz_pg, sz_pe, sz_pi};
+  for (int i = 0; i < 6; ++i) {
+    off[i] = o;
+    memcpy(blob.data() + o, src[i], sz[i]);
+    o += al(sz[i]);
+  }
+
+  ntt_ks_plan* p = new (std::nothrow) ntt_ks_plan;
+  if (!p) return NTT_ENOMEM;
+  {
+    DeviceGuard g(qp->device);
+    if (!g.ok) {
+      delete p;
+      return NTT_EDEVICE;
+    }
+    if (hipMalloc(&p->d_const, total) != hipSuccess) {
+      delete p;
+      return NTT_ENOMEM;
+    }
+    if (hipMemcpy(p->d_const, blob.data(), total, hipMemcpyHostToDevice) != hipSuccess) {
+      (void)hipFree(p->d_const);
+      delete p;
+      return NTT_EDEVICE;
+    }
+  }
+  uint8_t* base = (uint8_t*)p->d_const;
+  p->qp = qp;
+  p->nq = nq;
+  p->np = np_;
+  p->dnum = dnum;
+  p->alpha = alpha;
+  p->dev.moduli = (const uint64_t*)(base + off[0]);
+  p->dev.digit_garner = (const Tw*)(base + off[1]);
+  p->dev.digit_eval = (const Tw*)(base + off[2]);
+  p->dev.p_garner = (const Tw*)(base + off[3]);
+  p->dev.p_eval = (const Tw*)(base + off[4]);
+  p->dev.p_inv = (const Tw*)(base + off[5]);
+  *out = p;
+  return NTT_OK;
+}
+
+static uint64_t ws_elems(const ntt_ks_plan* p, uint64_t batch) {
+  return batch * (uint64_t)(p->dnum + 2) * (p->nq + p->np) * p->qp->n;
+}
+
+extern "C" int keyswitch_workspace_size(const ntt_ks_plan* p, uint64_t batch, size_t* bytes) {
+  if (!p || !bytes) return NTT_EINVAL;
+  if (batch > 4096) return NTT_EUNSUPPORTED;
+  *bytes = (size_t)ws_elems(p, batch) * 8;
+  return NTT_OK;
+}
+
+namespace {
+bool ranges_overlap(const void* a, uint64_t na, const void* b, uint64_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return na && nb && x < y + nb && y < x + na;
+}
+}  // namespace
+
+extern "C" int keyswitch(const ntt_ks_plan* p, uint64_t* out, const uint64_t* ct, const uint64_t* ksk,
+                         uint64_t galois_elt, uint64_t batch, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!p) return NTT_EINVAL;
+  const ntt_plan* qp = p->qp;
+  const uint32_t n = qp->n, nq = p->nq, np_ = p->np, nqp = nq + np_, dnum = p->dnum;
+  if (!(galois_elt & 1) || galois_elt >= 2ull * n) return NTT_EINVAL;
+  if (batch == 0) return NTT_OK;
+  if (batch > 4096) return NTT_EUNSUPPORTED;
+  if (!out || !ct || !ksk || !workspace) return NTT_EINVAL;
+  if (((uintptr_t)out | (uintptr_t)ct | (uintptr_t)ksk) & 15u) return NTT_EINVAL;
+  if ((uintptr_t)workspace & 255u) return NTT_EINVAL;
+  const uint64_t need = ws_elems(p, batch) * 8;
+  if (workspace_bytes < need) return NTT_EINVAL;
+  const uint64_t ct_bytes = batch * 2ull * nq * n * 8, ksk_bytes = (uint64_t)dnum * 2 * nqp * n * 8;
+  if (ranges_overlap(out, ct_bytes, ct, ct_bytes) || ranges_overlap(out, ct_bytes, ksk, ksk_bytes) ||
+      ranges_overlap(out, ct_bytes, workspace, need) || ranges_overlap(workspace, need, ct, ct_bytes) ||
+      ranges_overlap(workspace, need, ksk, ksk_bytes))
+    return NTT_EOVERLAP;
+
+  DeviceGuard g(qp->device);
+  if (!g.ok) return NTT_EDEVICE;
+  hipStream_t s = (hipStream_t)stream;
+  uint64_t* ext = (uint64_t*)workspace;
+  uint64_t* acc = ext + batch * (uint64_t)dnum * nqp * n;
+  const uint32_t two_n = 2 * n;
+  const uint32_t h = (uint32_t)host_invmod(galois_elt % two_n, two_n);
+  const uint32_t tiles = (n + kKsThreads - 1) / kKsThreads;
+
+  if (p->alpha <= 8)
+    hipLaunchKernelGGL((modup_kernel<8>), dim3(tiles, (uint32_t)(batch * dnum)), dim3(kKsThreads), 0, s, ext, ct,
+                       p->dev, qp->logn, h, nq, np_, p->alpha, dnum);
+  else
+    hipLaunchKernelGGL((modup_kernel<16>), dim3(tiles, (uint32_t)(batch * dnum)), dim3(kKsThreads), 0, s, ext, ct,
+                       p->dev, qp->logn, h, nq, np_, p->alpha, dnum);
+  if (hipGetLastError() != hipSuccess) return NTT_EDEVICE;
+  if (launch_ntt(qp, ext, batch * dnum, 0, nqp, false, s) != hipSuccess) return NTT_EDEVICE;
+  const uint64_t pairs = (uint64_t)nqp * n / 2;
+  hipLaunchKernelGGL(mac_kernel, dim3((uint32_t)((pairs + kKsThreads - 1) / kKsThreads), (uint32_t)batch),
+                     dim3(kKsThreads), 0, s, acc, ext, ksk, qp->d_mods, qp->logn, nqp, dnum, pairs);
+  if (hipGetLastError() != hipSuccess) return NTT_EDEVICE;
+  if (launch_ntt(qp, acc, batch * 2, 0, nqp, true, s) != hipSuccess) return NTT_EDEVICE;
+  if (np_ <= 8)
+    hipLaunchKernelGGL((moddown_kernel<8>), dim3(tiles, (uint32_t)(batch * 2)), dim3(kKsThreads), 0, s, out, acc, ct,
+                       p->dev, qp->logn, h, nq, np_);
+  else
+    hipLaunchKernelGGL((moddown_kernel<16>), dim3(tiles, (uint32_t)(batch * 2)), dim3(kKsThreads), 0, s, out, acc,
+                       ct, p->dev, qp->logn, h, nq, np_);
+  return hipGetLastError() == hipSuccess ? NTT_OK : NTT_EDEVICE;
+}
+
+extern "C" void keyswitch_plan_destroy(ntt_ks_plan* p) {
+  if (!p) return;
+  if (p->d_const) {
+    DeviceGuard g(p->qp->device);
+    (void)hipFree(p->d_const);
+  }
+  delete p;
+}

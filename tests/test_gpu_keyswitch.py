@@ -1,0 +1,138 @@
+"""GPU parity: the rotation key-switch vs the oracle (bit-exact), plus its special
+cases and the semantic check with a real key at a small ring."""
+import numpy as np
+import pytest
+
+import oracle as orc
+from negacyclic_ntt_amd import inputs, workloads
+from tests.helpers import announce, assert_bits_equal, dev, host, primes, require_gpu, residues
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    require_gpu()
+    from negacyclic_ntt_amd import binding
+    return binding
+
+
+def _setup(B, n, nq=24, npr=8, dnum=3):
+    qp = list(primes(60, 1 << 17, nq + npr))
+    plan = B.Plan(n, qp, 0)
+    ks = B.KeySwitchPlan(plan, nq, npr, dnum)
+    return qp, plan, ks
+
+
+@pytest.mark.parametrize("g", [5, 25, 65537, 1, 2 * 65536 - 1])
+def test_keyswitch_workload_vs_oracle(B, g):
+    w = workloads.KEYSWITCH
+    qp, plan, ks = _setup(B, w.n)
+    ct = residues(w.shape_a, qp[:24], w.seed_a)
+    ksk = residues((3, 2, 32, w.n), qp, w.seed_b)
+    announce("keyswitch workload", g)
+    out = B.keyswitch(ks, dev(np.zeros_like(ct)), dev(ct), dev(ksk), g)
+    want = orc.keyswitch(ct, ksk, g, qp, 24, 3)
+    assert_bits_equal(host(out), want, f"keyswitch g={g}")
+
+
+@pytest.mark.parametrize("logn,nq,npr,dnum", [(10, 24, 8, 3), (12, 6, 2, 2), (11, 16, 16, 1), (3, 4, 3, 4),
+                                              (13, 12, 5, 3)])
+def test_keyswitch_shapes_vs_oracle(B, logn, nq, npr, dnum):
+    n = 1 << logn
+    qp, plan, ks = _setup(B, n, nq, npr, dnum)
+    ct = residues((2, 2, nq, n), qp[:nq], 9500 + logn)
+    ksk = residues((dnum, 2, nq + npr, n), qp[: nq + npr], 9600 + logn)
+    g = 5 % (2 * n)
+    announce("keyswitch shape", logn, nq, npr, dnum)
+    out = B.keyswitch(ks, dev(np.zeros_like(ct)), dev(ct), dev(ksk), g)
+    assert_bits_equal(host(out), orc.keyswitch(ct, ksk, g, qp[: nq + npr], nq, dnum), "keyswitch shape")
+
+
+def test_keyswitch_zero_key_and_zero_c1(B):
+    n = 1 << 12
+    qp, plan, ks = _setup(B, n)
+    ct = residues((1, 2, 24, n), qp[:24], 9700)
+    g = 25
+    sig = orc.batch_automorph(ct[0], g, 0, qp[:24])
+    announce("keyswitch zero key")
+    out = host(B.keyswitch(ks, dev(np.zeros_like(ct)), dev(ct), dev(np.zeros((3, 2, 32, n), np.uint64)), g))
+    assert_bits_equal(out[0, 0], sig[0], "ksk = 0 -> sigma(c0)")
+    assert not out[0, 1].any()
+    ct1 = ct.copy()
+    ct1[0, 1] = 0
+    ksk = residues((3, 2, 32, n), qp, 9701)
+    out = host(B.keyswitch(ks, dev(np.zeros_like(ct)), dev(ct1), dev(ksk), g))
+    assert_bits_equal(out[0, 0], sig[0], "c1 = 0 -> sigma(c0)")
+    assert not out[0, 1].any()
+
+
+def test_keyswitch_semantic_small_ring(B):
+    """With a real key at n = 1024 the switched ciphertext decrypts, under s, to what
+    sigma_g of the input decrypts to under sigma_g(s), up to a small error."""
+    n, g, dnum, alpha = 1024, 5, 3, 8
+    qp, plan, ks = _setup(B, n)
+    Q, P = qp[:24], qp[24:]
+    s = inputs.small_signed(n, 1, 130)
+    s_limbs = np.array([[int(v) % q for v in s] for q in qp], dtype=np.uint64)
+    s_rot = orc.batch_automorph(s_limbs, g, 0, qp)
+    Pm = 1
+    for p in P:
+        Pm *= p
+
+    def pmul(a, b, ps):
+        return orc.batch_ntt(orc.batch_pointwise(orc.batch_ntt(a, ps), orc.batch_ntt(b, ps), ps), ps, inverse=True)
+
+    ksk = np.zeros((dnum, 2, 32, n), dtype=np.uint64)
+    for j in range(dnum):
+        a_j = residues((32, n), qp, 140 + j)
+        e = inputs.small_signed(n, 8, 150 + j)
+        e_j = np.array([[int(v) % q for v in e] for q in qp], dtype=np.uint64)
+        as_ = pmul(a_j, s_limbs, qp)
+        b_coef = np.zeros((32, n), dtype=np.uint64)
+        for l, q in enumerate(qp):
+            pts = (s_rot[l].astype(object) * (Pm % q)) % q if j * alpha <= l < (j + 1) * alpha else 0
+            b_coef[l] = ((e_j[l].astype(object) - as_[l].astype(object) + pts) % q).astype(np.uint64)
+        ksk[j, 0] = orc.batch_ntt(b_coef, qp)
+        ksk[j, 1] = orc.batch_ntt(a_j, qp)
+    ct = residues((1, 2, 24, n), Q, 160)
+    announce("keyswitch semantic")
+    out = host(B.keyswitch(ks, dev(np.zeros_like(ct)), dev(ct), dev(ksk), g))
+    assert_bits_equal(out, orc.keyswitch(ct, ksk, g, qp, 24, dnum), "semantic-key case vs oracle")
+    lhs = out[0, 0].astype(object) + pmul(out[0, 1], s_limbs[:24], Q).astype(object)
+    c_rot = orc.batch_automorph(ct[0], g, 0, Q)
+    rhs = c_rot[0].astype(object) + pmul(c_rot[1], s_rot[:24], Q).astype(object)
+    from sympy.ntheory.modular import crt
+    Qm = 1
+    for q in Q:
+        Qm *= q
+    worst = 0
+    for i in range(0, n, 7):
+        v = int(crt(Q, [int((lhs[l][i] - rhs[l][i]) % Q[l]) for l in range(24)])[0])
+        v = v - Qm if v > Qm // 2 else v
+        worst = max(worst, abs(v))
+    assert worst < (1 << 20), worst
+
+
+def test_keyswitch_validation(B):
+    import ctypes
+    import torch
+    n = 1 << 10
+    qp, plan, ks = _setup(B, n)
+    L = B.lib()
+    ct = torch.zeros((1, 2, 24, n), dtype=torch.int64, device="cuda:0")
+    out = torch.zeros_like(ct)
+    ksk = torch.zeros((3, 2, 32, n), dtype=torch.int64, device="cuda:0")
+    ws = B.workspace(ks, 1)
+    V = ctypes.c_void_p
+    args = (V(out.data_ptr()), V(ct.data_ptr()), V(ksk.data_ptr()))
+    nb = ws.numel()
+    assert L.keyswitch(ks.handle, *args, 4, 1, V(ws.data_ptr()), nb, None) == B.NTT_EINVAL     # even g
+    assert L.keyswitch(ks.handle, *args, 5, 1, V(ws.data_ptr()), nb - 1, None) == B.NTT_EINVAL  # small ws
+    assert L.keyswitch(ks.handle, V(ct.data_ptr()), V(ct.data_ptr()), V(ksk.data_ptr()), 5, 1, V(ws.data_ptr()), nb,
+                       None) == B.NTT_EOVERLAP
+    assert L.keyswitch(ks.handle, *args, 5, 1, V(ct.data_ptr()), nb, None) == B.NTT_EOVERLAP
+    h = V()
+    assert L.keyswitch_plan_create(ctypes.byref(h), plan.handle, 24, 8, 5) == B.NTT_EINVAL  # 24 % 5
+    assert L.keyswitch_plan_create(ctypes.byref(h), plan.handle, 24, 9, 3) == B.NTT_EINVAL  # beyond the plan
+    assert L.keyswitch_plan_create(ctypes.byref(h), plan.handle, 24, 8, 1) == B.NTT_EUNSUPPORTED  # alpha 24

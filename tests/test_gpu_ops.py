@@ -1,0 +1,186 @@
+"""GPU parity: pointwise product, tensor product and automorphisms vs the oracle;
+device-side argument validation."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle as orc
+from negacyclic_ntt_amd import workloads
+from tests.helpers import announce, assert_bits_equal, dev, host, primes, require_gpu, residues
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    require_gpu()
+    from negacyclic_ntt_amd import binding
+    return binding
+
+
+def test_polymul_workload_vs_oracle_and_schoolbook(B):
+    w = workloads.POLYMUL
+    ps = primes(w.bits, 2 * w.n, w.limbs)
+    a = residues(w.shape_a, ps, w.seed_a)
+    b = residues(w.shape_a, ps, w.seed_b)
+    plan = B.Plan(w.n, ps, 0)
+    ta, tb = dev(a), dev(b)
+    announce("polymul workload")
+    B.ntt_forward(plan, ta)
+    B.ntt_forward(plan, tb)
+    tc = B.poly_mul_ntt(plan, ta.clone(), ta, tb)
+    B.ntt_inverse(plan, tc)
+    got = host(tc)
+    for l, q in enumerate(ps):
+        assert_bits_equal(got[l], orc.schoolbook(a[l], b[l], q), f"limb {l} vs schoolbook")
+
+
+@pytest.mark.parametrize("bits,logn", [(30, 11), (60, 14), (62, 16), (31, 5)])
+def test_pointwise_in_and_out_of_place(B, bits, logn):
+    n = 1 << logn
+    ps = primes(bits, 1 << 17, 3)
+    plan = B.Plan(n, ps, 0)
+    a = residues((5, 3, n), ps, 9000 + logn)
+    b = residues((5, 3, n), ps, 9100 + logn)
+    want = orc.batch_pointwise(a, b, ps)
+    announce("pointwise", bits, logn)
+    ta, tb = dev(a), dev(b)
+    out = B.poly_mul_ntt(plan, dev(np.zeros_like(a)), ta, tb)
+    assert_bits_equal(host(out), want, "out of place")
+    B.poly_mul_ntt(plan, ta, ta, tb)
+    assert_bits_equal(host(ta), want, "out == a")
+    tb2 = dev(b)
+    B.poly_mul_ntt(plan, tb2, dev(a), tb2)
+    assert_bits_equal(host(tb2), want, "out == b")
+    # extreme residues: (q-1)^2
+    m = np.array([[[q - 1] * n for q in ps]], dtype=np.uint64)
+    assert_bits_equal(host(B.poly_mul_ntt(plan, dev(m), dev(m), dev(m))), orc.batch_pointwise(m, m, ps), "q-1")
+
+
+def test_batch_workload_pipeline(B):
+    """n = 2^14 throughput batch: NTT(A), pointwise with B, inverse NTT."""
+    w = workloads.BATCH
+    ps = primes(w.bits, 2 * w.n, w.limbs)
+    a = residues(w.shape_a, ps, w.seed_a)
+    b = residues(w.shape_a, ps, w.seed_b)
+    plan = B.Plan(w.n, ps, 0)
+    announce("batch workload pipeline")
+    ta = dev(a)
+    B.ntt_forward(plan, ta)
+    B.poly_mul_ntt(plan, ta, ta, dev(b))
+    B.ntt_inverse(plan, ta)
+    want = orc.batch_ntt(orc.batch_pointwise(orc.batch_ntt(a, ps), b, ps), ps, inverse=True)
+    assert_bits_equal(host(ta), want, w.name)
+
+
+def test_tensor_chain_workload(B):
+    w = workloads.CHAIN
+    ps = primes(w.bits, 2 * w.n, w.limbs)
+    a = residues(w.shape_a, ps, w.seed_a)
+    b = residues(w.shape_a, ps, w.seed_b)
+    plan = B.Plan(w.n, ps, 0)
+    announce("tensor chain workload")
+    ta, tb = dev(a), dev(b)
+    B.ntt_forward(plan, ta)
+    B.ntt_forward(plan, tb)
+    import torch
+    d = torch.empty((4, 3, w.limbs, w.n), dtype=torch.int64, device="cuda:0")
+    B.ct_tensor_ntt(plan, d, ta, tb)
+    ah, bh = orc.batch_ntt(a, ps), orc.batch_ntt(b, ps)
+    want = orc.batch_tensor(ah, bh, ps)
+    assert_bits_equal(host(d), want, "tensor d0,d1,d2")
+    # inverse of d (1344 limb-INTTs) back to the coefficient domain
+    B.ntt_inverse(plan, d)
+    assert_bits_equal(host(d), orc.batch_ntt(want, ps, inverse=True), "inverse of the tensor")
+
+
+def test_tensor_limb_subrange(B):
+    ps = primes(60, 1 << 13, 6)
+    n = 4096
+    plan = B.Plan(n, ps, 0)
+    sub = ps[2:5]
+    a = residues((3, 2, 3, n), sub, 9300)
+    b = residues((3, 2, 3, n), sub, 9301)
+    import torch
+    d = torch.empty((3, 3, 3, n), dtype=torch.int64, device="cuda:0")
+    announce("tensor subrange")
+    B.ct_tensor_ntt(plan, d, dev(a), dev(b), limb_begin=2)
+    assert_bits_equal(host(d), orc.batch_tensor(a, b, sub), "tensor limbs 2..4")
+
+
+@pytest.mark.parametrize("domain", [0, 1])
+def test_automorph_ring_workload_all_galois(B, domain):
+    w = workloads.RING
+    ps = primes(w.bits, 2 * w.n, w.limbs)
+    x = residues((1, 2, w.limbs, w.n), ps, w.seed_a)
+    plan = B.Plan(w.n, ps, 0)
+    tx = dev(x)
+    import torch
+    out = torch.empty_like(tx)
+    for g in w.galois:
+        announce("automorph", domain, g)
+        B.automorph(plan, out, tx, g, domain)
+        assert_bits_equal(host(out), orc.batch_automorph(x, g, domain, ps), f"automorph g={g} domain={domain}")
+
+
+def test_automorph_full_batch_and_ntt_commutation(B):
+    w = workloads.RING
+    ps = primes(w.bits, 2 * w.n, w.limbs)
+    x = residues(w.shape_a, ps, w.seed_a)
+    plan = B.Plan(w.n, ps, 0)
+    import torch
+    tx = dev(x)
+    out = torch.empty_like(tx)
+    g = w.galois[0]
+    announce("automorph full batch")
+    B.automorph(plan, out, tx, g, 0)
+    assert_bits_equal(host(out), orc.batch_automorph(x, g, 0, ps), "full batch")
+    # NTT(sigma_g a) == automorph_ntt(NTT a) on the device
+    B.ntt_forward(plan, out)
+    fx = B.ntt_forward(plan, tx)
+    out2 = torch.empty_like(fx)
+    B.automorph(plan, out2, fx, g, 1)
+    assert_bits_equal(host(out), host(out2), "NTT-domain automorph commutes with the NTT")
+
+
+@pytest.mark.parametrize("logn", [1, 2, 5, 10, 13])
+def test_automorph_small_rings(B, logn):
+    n = 1 << logn
+    ps = primes(30, 1 << 17, 2)
+    plan = B.Plan(n, ps, 0)
+    x = residues((3, 2, n), ps, 9400 + logn)
+    tx = dev(x)
+    import torch
+    out = torch.empty_like(tx)
+    for g in sorted({1, 3 % (2 * n) or 1, 5 % (2 * n) or 1, 2 * n - 1}):
+        for domain in (0, 1):
+            B.automorph(plan, out, tx, g, domain)
+            assert_bits_equal(host(out), orc.batch_automorph(x, g, domain, ps), f"n={n} g={g} d={domain}")
+
+
+def test_device_validation(B):
+    import torch
+    ps = primes(60, 1 << 12, 2)
+    plan = B.Plan(2048, ps, 0)
+    L = B.lib()
+    t = torch.zeros((2, 2, 2048), dtype=torch.int64, device="cuda:0")
+    p = ctypes.c_void_p(t.data_ptr())
+    half = ctypes.c_void_p(t.data_ptr() + 8 * 2048)  # partial overlap with t
+    mis = ctypes.c_void_p(t.data_ptr() + 8)           # 8-byte misaligned
+    assert L.ntt_forward(plan.handle, mis, 1, 0, 2, None) == B.NTT_EINVAL
+    assert L.ntt_forward(plan.handle, p, 1, 1, 2, None) == B.NTT_EINVAL       # limb range beyond the plan
+    assert L.ntt_forward(plan.handle, p, 1, 0, 0, None) == B.NTT_EINVAL
+    assert L.poly_mul_ntt(plan.handle, half, p, p, 1, 0, 2, None) == B.NTT_EOVERLAP
+    assert L.automorph(plan.handle, p, p, 5, 0, 1, 0, 2, None) == B.NTT_EOVERLAP
+    assert L.automorph(plan.handle, half, p, 4, 0, 1, 0, 2, None) == B.NTT_EINVAL   # even g
+    assert L.automorph(plan.handle, half, p, 4097, 0, 1, 0, 2, None) == B.NTT_EINVAL  # g >= 2n
+    assert L.automorph(plan.handle, half, p, 5, 2, 1, 0, 2, None) == B.NTT_EINVAL   # bad domain
+    assert L.ct_tensor_ntt(plan.handle, p, p, p, 1, 0, 2, None) == B.NTT_EOVERLAP
+    assert L.ntt_forward_galois(plan.handle, half, p, 5, 1, 0, 2, None) == B.NTT_EOVERLAP
+    with pytest.raises(TypeError):
+        B.ntt_forward(plan, t.to(torch.int32))
+    with pytest.raises(ValueError):
+        B.ntt_forward(plan, t[:, :, :1024])
+    with pytest.raises(ValueError):
+        B.ntt_forward(plan, t.transpose(0, 1))
