@@ -173,12 +173,17 @@ struct LdsCfg {
   static constexpr int ROWS = (NT << RMAX) / N;
 };
 
-template <class A, int LOGN, bool FWD>
-__global__ __launch_bounds__(LdsCfg<LOGN>::NT) void ntt_lds_kernel(uint64_t* __restrict__ data,
+// GAL: the coefficient-domain automorphism sigma_g is applied while loading
+// (residue i of `in` lands, negated when i*g mod 2n >= n, at slot i*g mod n of
+// the LDS row), so that the launch computes NTT(sigma_g(in)).  `in` may equal
+// `data`: every row is fully loaded before any store.
+template <class A, int LOGN, bool FWD, bool GAL>
+__global__ __launch_bounds__(LdsCfg<LOGN>::NT) void ntt_lds_kernel(uint64_t* data,
+                                                                   const uint64_t* in,
                                                                    const void* __restrict__ tw_all,
                                                                    const ModInfo* __restrict__ mods,
                                                                    uint32_t num_limbs, uint32_t limb_begin,
-                                                                   uint64_t total_rows) {
+                                                                   uint64_t total_rows, uint32_t galois) {
   using T = typename A::T;
   using C = LdsCfg<LOGN>;
   constexpr int N = C::N, ROWS = C::ROWS, NT = C::NT;
@@ -191,9 +196,18 @@ __global__ __launch_bounds__(LdsCfg<LOGN>::NT) void ntt_lds_kernel(uint64_t* __r
   for (int e = 2 * tid; e < ROWS * N; e += 2 * NT) {
     const int sub = e / N, pos = e % N;
     if (row0 + sub < total_rows) {
-      const ulonglong2 v = *reinterpret_cast<const ulonglong2*>(data + (row0 + sub) * N + pos);
-      lds[sub * STRIDE + lpos<A>(pos)] = (T)v.x;
-      lds[sub * STRIDE + lpos<A>(pos + 1)] = (T)v.y;
+      const ulonglong2 v = *reinterpret_cast<const ulonglong2*>(in + (row0 + sub) * N + pos);
+      if (GAL) {
+        const T q = (T)mods[limb_begin + (uint32_t)((row0 + sub) % num_limbs)].q;
+        const uint32_t e0 = (uint32_t)(((uint64_t)pos * galois) & (2 * N - 1));
+        const uint32_t e1 = (uint32_t)(((uint64_t)(pos + 1) * galois) & (2 * N - 1));
+        const T x0 = (T)v.x, x1 = (T)v.y;
+        lds[sub * STRIDE + lpos<A>(e0 & (N - 1))] = e0 >= (uint32_t)N ? (x0 ? q - x0 : x0) : x0;
+        lds[sub * STRIDE + lpos<A>(e1 & (N - 1))] = e1 >= (uint32_t)N ? (x1 ? q - x1 : x1) : x1;
+      } else {
+        lds[sub * STRIDE + lpos<A>(pos)] = (T)v.x;
+        lds[sub * STRIDE + lpos<A>(pos + 1)] = (T)v.y;
+      }
     }
   }
   __syncthreads();
@@ -238,12 +252,37 @@ struct RowCfg {
   static constexpr int NT = (kRows << LOGN2) >> S.r[0];
 };
 
+// Row permutation of the NTT-domain automorphism on an N1 x N2 slot grid.  Slot
+// k = r N2 + c evaluates at psi^(2 brv(k) + 1) and 2 brv(k) + 1 mod 2 N1 depends
+// on r only, so NTT(sigma_g a)[r N2 + c] = NTT(a)[rp(r) N2 + cp(r, c)] with
+//   2 brv(rp) + 1 = g (2 brv(r) + 1)  (mod 2 N1),
+//   cp = brv_{log N2}( (g (2 brv(k) + 1) mod 2N) >> (log N1 + 1) ).
+template <int LOGB>
+__device__ __forceinline__ uint32_t brv_bits(uint32_t x) {
+  return __brev(x) >> (32 - LOGB);
+}
+template <int LOGN1>
+__device__ __forceinline__ uint32_t galois_row(uint32_t r, uint32_t g) {
+  const uint32_t f = (g * (2 * brv_bits<LOGN1>(r) + 1)) & ((2u << LOGN1) - 1);
+  return brv_bits<LOGN1>(f >> 1);
+}
+template <int LOGN1, int LOGN2>
+__device__ __forceinline__ uint32_t galois_col(uint32_t r, uint32_t c, uint32_t g) {
+  const uint32_t k = (r << LOGN2) | c;
+  const uint32_t f = (uint32_t)(((uint64_t)g * (2 * brv_bits<LOGN1 + LOGN2>(k) + 1)) & ((2u << (LOGN1 + LOGN2)) - 1));
+  return brv_bits<LOGN2>(f >> (LOGN1 + 1));
+}
+
 // LAST: this launch finishes the transform (canonical output; inverse scaling).
-template <class A, int LOGN1, int LOGN2, bool FWD, bool LAST>
-__global__ __launch_bounds__(ColCfg<LOGN1>::NT) void ntt_col_kernel(uint64_t* __restrict__ data,
+// GAL (forward only): intermediate row rho is written to row slot galois_row(rho, h),
+// h = g^-1, i.e. the slot whose source row under g is rho; `in` may equal `data`.
+template <class A, int LOGN1, int LOGN2, bool FWD, bool LAST, bool GAL>
+__global__ __launch_bounds__(ColCfg<LOGN1>::NT) void ntt_col_kernel(uint64_t* data,
+                                                                    const uint64_t* in,
                                                                     const void* __restrict__ tw_all,
                                                                     const ModInfo* __restrict__ mods,
-                                                                    uint32_t num_limbs, uint32_t limb_begin) {
+                                                                    uint32_t num_limbs, uint32_t limb_begin,
+                                                                    uint32_t galois_inv) {
   using T = typename A::T;
   constexpr int N1 = 1 << LOGN1, N2 = 1 << LOGN2, N = N1 * N2;
   constexpr int NT = ColCfg<LOGN1>::NT;
@@ -255,10 +294,11 @@ __global__ __launch_bounds__(ColCfg<LOGN1>::NT) void ntt_col_kernel(uint64_t* __
   const int c0 = (blockIdx.x % BLOCKS_PER_LIMB) * kCols;
   const uint32_t limb = limb_begin + (uint32_t)(row % num_limbs);
   uint64_t* base = data + row * N + c0;
+  const uint64_t* src = in + row * N + c0;
 
   for (int e = 2 * tid; e < kCols * N1; e += 2 * NT) {
     const int rr = e / kCols, c = e % kCols;
-    const ulonglong2 v = *reinterpret_cast<const ulonglong2*>(base + (size_t)rr * N2 + c);
+    const ulonglong2 v = *reinterpret_cast<const ulonglong2*>(src + (size_t)rr * N2 + c);
     lds[c * STRIDE + lpos<A>(rr)] = (T)v.x;
     lds[(c + 1) * STRIDE + lpos<A>(rr)] = (T)v.y;
   }
@@ -282,15 +322,19 @@ __global__ __launch_bounds__(ColCfg<LOGN1>::NT) void ntt_col_kernel(uint64_t* __
       v.x = A::widen(lds[c * STRIDE + lpos<A>(rr)]);
       v.y = A::widen(lds[(c + 1) * STRIDE + lpos<A>(rr)]);
     }
-    *reinterpret_cast<ulonglong2*>(base + (size_t)rr * N2 + c) = v;
+    const uint32_t slot = GAL ? galois_row<LOGN1>((uint32_t)rr, galois_inv) : (uint32_t)rr;
+    *reinterpret_cast<ulonglong2*>(base + (size_t)slot * N2 + c) = v;
   }
 }
 
-template <class A, int LOGN1, int LOGN2, bool FWD, bool LAST>
+// GAL (forward only): row slot r holds intermediate row galois_row(r, g); the
+// output of slot r is that row's transform permuted by galois_col.
+template <class A, int LOGN1, int LOGN2, bool FWD, bool LAST, bool GAL>
 __global__ __launch_bounds__(RowCfg<LOGN2>::NT) void ntt_row_kernel(uint64_t* __restrict__ data,
                                                                     const void* __restrict__ tw_all,
                                                                     const ModInfo* __restrict__ mods,
-                                                                    uint32_t num_limbs, uint32_t limb_begin) {
+                                                                    uint32_t num_limbs, uint32_t limb_begin,
+                                                                    uint32_t galois) {
   using T = typename A::T;
   constexpr int N1 = 1 << LOGN1, N2 = 1 << LOGN2, N = N1 * N2;
   constexpr int NT = RowCfg<LOGN2>::NT;
@@ -318,7 +362,7 @@ __global__ __launch_bounds__(RowCfg<LOGN2>::NT) void ntt_row_kernel(uint64_t* __
     SubParams<A> sp;
     sp.tw = tw;
     sp.q = q;
-    sp.prefix = (uint32_t)(N1 + r0 + sub);
+    sp.prefix = (uint32_t)N1 + (GAL ? galois_row<LOGN1>((uint32_t)(r0 + sub), galois) : (uint32_t)(r0 + sub));
     return sp;
   };
   run_passes<A, FWD, LOGN2, kRows, NT, 0>(lds, tid, get_sub);
@@ -326,7 +370,13 @@ __global__ __launch_bounds__(RowCfg<LOGN2>::NT) void ntt_row_kernel(uint64_t* __
   for (int e = 2 * tid; e < kRows * N2; e += 2 * NT) {
     const int sub = e / N2, pos = e % N2;
     ulonglong2 v;
-    if (LAST) {
+    if (GAL) {
+      const uint32_t r = (uint32_t)(r0 + sub);
+      const int p0 = (int)galois_col<LOGN1, LOGN2>(r, (uint32_t)pos, galois);
+      const int p1 = (int)galois_col<LOGN1, LOGN2>(r, (uint32_t)pos + 1, galois);
+      v.x = finish<A, FWD>(lds[sub * STRIDE + lpos<A>(p0)], m);
+      v.y = finish<A, FWD>(lds[sub * STRIDE + lpos<A>(p1)], m);
+    } else if (LAST) {
       v.x = finish<A, FWD>(lds[sub * STRIDE + lpos<A>(pos)], m);
       v.y = finish<A, FWD>(lds[sub * STRIDE + lpos<A>(pos + 1)], m);
     } else {
@@ -338,50 +388,69 @@ __global__ __launch_bounds__(RowCfg<LOGN2>::NT) void ntt_row_kernel(uint64_t* __
 }
 
 // ---------------------------------------------------------------------------
+// What one launch sequence computes.
+enum class Op { kForward, kInverse, kForwardGalois };
+
+template <class A>
+const void* tables_for(const ntt_plan* p, Op op) {
+  const bool inv = op == Op::kInverse;
+  if (sizeof(typename A::T) == 8) return inv ? (const void*)p->d_inv : (const void*)p->d_fwd;
+  return inv ? (const void*)p->d_inv32 : (const void*)p->d_fwd32;
+}
+
 template <class A, int LOGN>
-hipError_t launch_lds(const ntt_plan* p, uint64_t* data, uint64_t rows, uint32_t limb_begin, uint32_t num_limbs,
-                      bool inverse, hipStream_t s) {
+hipError_t launch_lds(const ntt_plan* p, uint64_t* data, const uint64_t* in, uint64_t rows, uint32_t limb_begin,
+                      uint32_t num_limbs, Op op, uint32_t g, hipStream_t s) {
   using C = LdsCfg<LOGN>;
-  const void* tw = sizeof(typename A::T) == 8 ? (inverse ? (const void*)p->d_inv : (const void*)p->d_fwd)
-                                              : (inverse ? (const void*)p->d_inv32 : (const void*)p->d_fwd32);
+  const void* tw = tables_for<A>(p, op);
   const uint64_t blocks = (rows + C::ROWS - 1) / C::ROWS;
-  if (inverse)
-    hipLaunchKernelGGL((ntt_lds_kernel<A, LOGN, false>), dim3((uint32_t)blocks), dim3(C::NT), 0, s, data, tw,
-                       p->d_mods, num_limbs, limb_begin, rows);
+  const dim3 grid((uint32_t)blocks), block(C::NT);
+  if (op == Op::kInverse)
+    hipLaunchKernelGGL((ntt_lds_kernel<A, LOGN, false, false>), grid, block, 0, s, data, in, tw, p->d_mods,
+                       num_limbs, limb_begin, rows, 1u);
+  else if (op == Op::kForward)
+    hipLaunchKernelGGL((ntt_lds_kernel<A, LOGN, true, false>), grid, block, 0, s, data, in, tw, p->d_mods,
+                       num_limbs, limb_begin, rows, 1u);
   else
-    hipLaunchKernelGGL((ntt_lds_kernel<A, LOGN, true>), dim3((uint32_t)blocks), dim3(C::NT), 0, s, data, tw,
-                       p->d_mods, num_limbs, limb_begin, rows);
+    hipLaunchKernelGGL((ntt_lds_kernel<A, LOGN, true, true>), grid, block, 0, s, data, in, tw, p->d_mods,
+                       num_limbs, limb_begin, rows, g);
   return hipGetLastError();
 }
 
 template <class A, int LOGN1, int LOGN2>
-hipError_t launch_split(const ntt_plan* p, uint64_t* data, uint64_t rows, uint32_t limb_begin, uint32_t num_limbs,
-                        bool inverse, hipStream_t s) {
-  const void* tw = sizeof(typename A::T) == 8 ? (inverse ? (const void*)p->d_inv : (const void*)p->d_fwd)
-                                              : (inverse ? (const void*)p->d_inv32 : (const void*)p->d_fwd32);
-  const uint32_t col_blocks = (uint32_t)(rows * ((1u << LOGN2) / kCols));
-  const uint32_t row_blocks = (uint32_t)(rows * ((1u << LOGN1) / kRows));
-  if (!inverse) {
-    hipLaunchKernelGGL((ntt_col_kernel<A, LOGN1, LOGN2, true, false>), dim3(col_blocks), dim3(ColCfg<LOGN1>::NT), 0,
-                       s, data, tw, p->d_mods, num_limbs, limb_begin);
-    hipLaunchKernelGGL((ntt_row_kernel<A, LOGN1, LOGN2, true, true>), dim3(row_blocks), dim3(RowCfg<LOGN2>::NT), 0,
-                       s, data, tw, p->d_mods, num_limbs, limb_begin);
+hipError_t launch_split(const ntt_plan* p, uint64_t* data, const uint64_t* in, uint64_t rows, uint32_t limb_begin,
+                        uint32_t num_limbs, Op op, uint32_t g, hipStream_t s) {
+  const void* tw = tables_for<A>(p, op);
+  const dim3 col_grid((uint32_t)(rows * ((1u << LOGN2) / kCols))), col_block(ColCfg<LOGN1>::NT);
+  const dim3 row_grid((uint32_t)(rows * ((1u << LOGN1) / kRows))), row_block(RowCfg<LOGN2>::NT);
+  if (op == Op::kForward) {
+    hipLaunchKernelGGL((ntt_col_kernel<A, LOGN1, LOGN2, true, false, false>), col_grid, col_block, 0, s, data, in,
+                       tw, p->d_mods, num_limbs, limb_begin, 1u);
+    hipLaunchKernelGGL((ntt_row_kernel<A, LOGN1, LOGN2, true, true, false>), row_grid, row_block, 0, s, data, tw,
+                       p->d_mods, num_limbs, limb_begin, 1u);
+  } else if (op == Op::kForwardGalois) {
+    const uint32_t two_n = 2u << (LOGN1 + LOGN2);
+    const uint32_t h = (uint32_t)host_invmod(g % two_n, two_n);
+    hipLaunchKernelGGL((ntt_col_kernel<A, LOGN1, LOGN2, true, false, true>), col_grid, col_block, 0, s, data, in,
+                       tw, p->d_mods, num_limbs, limb_begin, h);
+    hipLaunchKernelGGL((ntt_row_kernel<A, LOGN1, LOGN2, true, true, true>), row_grid, row_block, 0, s, data, tw,
+                       p->d_mods, num_limbs, limb_begin, g);
   } else {
-    hipLaunchKernelGGL((ntt_row_kernel<A, LOGN1, LOGN2, false, false>), dim3(row_blocks), dim3(RowCfg<LOGN2>::NT),
-                       0, s, data, tw, p->d_mods, num_limbs, limb_begin);
-    hipLaunchKernelGGL((ntt_col_kernel<A, LOGN1, LOGN2, false, true>), dim3(col_blocks), dim3(ColCfg<LOGN1>::NT), 0,
-                       s, data, tw, p->d_mods, num_limbs, limb_begin);
+    hipLaunchKernelGGL((ntt_row_kernel<A, LOGN1, LOGN2, false, false, false>), row_grid, row_block, 0, s, data, tw,
+                       p->d_mods, num_limbs, limb_begin, 1u);
+    hipLaunchKernelGGL((ntt_col_kernel<A, LOGN1, LOGN2, false, true, false>), col_grid, col_block, 0, s, data, data,
+                       tw, p->d_mods, num_limbs, limb_begin, 1u);
   }
   return hipGetLastError();
 }
 
 template <class A>
-hipError_t launch_any(const ntt_plan* p, uint64_t* data, uint64_t rows, uint32_t limb_begin, uint32_t num_limbs,
-                      bool inverse, hipStream_t s) {
+hipError_t launch_any(const ntt_plan* p, uint64_t* data, const uint64_t* in, uint64_t rows, uint32_t limb_begin,
+                      uint32_t num_limbs, Op op, uint32_t g, hipStream_t s) {
   switch (p->logn) {
 #define NNTT_CASE(L) \
   case L:            \
-    return launch_lds<A, L>(p, data, rows, limb_begin, num_limbs, inverse, s);
+    return launch_lds<A, L>(p, data, in, rows, limb_begin, num_limbs, op, g, s);
     NNTT_CASE(1)
     NNTT_CASE(2)
     NNTT_CASE(3)
@@ -398,12 +467,21 @@ hipError_t launch_any(const ntt_plan* p, uint64_t* data, uint64_t rows, uint32_t
     NNTT_CASE(14)
 #undef NNTT_CASE
     case 15:
-      return launch_split<A, 7, 8>(p, data, rows, limb_begin, num_limbs, inverse, s);
+      return launch_split<A, 7, 8>(p, data, in, rows, limb_begin, num_limbs, op, g, s);
     case 16:
-      return launch_split<A, 8, 8>(p, data, rows, limb_begin, num_limbs, inverse, s);
+      return launch_split<A, 8, 8>(p, data, in, rows, limb_begin, num_limbs, op, g, s);
     default:
       return hipErrorInvalidValue;
   }
+}
+
+hipError_t dispatch(const ntt_plan* p, uint64_t* data, const uint64_t* in, uint64_t batch, uint32_t limb_begin,
+                    uint32_t num_limbs, Op op, uint32_t g, hipStream_t s) {
+  const uint64_t rows = batch * num_limbs;
+  if (rows == 0) return hipSuccess;
+  if (range_is_narrow(p, limb_begin, num_limbs))
+    return launch_any<Narrow>(p, data, in, rows, limb_begin, num_limbs, op, g, s);
+  return launch_any<Wide>(p, data, in, rows, limb_begin, num_limbs, op, g, s);
 }
 
 }  // namespace
@@ -416,16 +494,12 @@ bool range_is_narrow(const ntt_plan* p, uint32_t limb_begin, uint32_t num_limbs)
 
 hipError_t launch_ntt(const ntt_plan* p, uint64_t* data, uint64_t batch, uint32_t limb_begin, uint32_t num_limbs,
                       bool inverse, hipStream_t s) {
-  const uint64_t rows = batch * num_limbs;
-  if (rows == 0) return hipSuccess;
-  if (range_is_narrow(p, limb_begin, num_limbs))
-    return launch_any<Narrow>(p, data, rows, limb_begin, num_limbs, inverse, s);
-  return launch_any<Wide>(p, data, rows, limb_begin, num_limbs, inverse, s);
+  return dispatch(p, data, data, batch, limb_begin, num_limbs, inverse ? Op::kInverse : Op::kForward, 1u, s);
 }
 
-hipError_t launch_ntt_galois(const ntt_plan*, uint64_t*, const uint64_t*, uint64_t, uint64_t, uint32_t, uint32_t,
-                             hipStream_t) {
-  return hipErrorNotSupported;
+hipError_t launch_ntt_galois(const ntt_plan* p, uint64_t* out, const uint64_t* in, uint64_t g, uint64_t batch,
+                             uint32_t limb_begin, uint32_t num_limbs, hipStream_t s) {
+  return dispatch(p, out, in, batch, limb_begin, num_limbs, Op::kForwardGalois, (uint32_t)(g % (2ull * p->n)), s);
 }
 
 }  // namespace nntt

@@ -124,3 +124,41 @@ def test_repeat_and_streams_bit_identical(B):
         B.ntt_forward(plan, b)
     torch.cuda.synchronize()
     assert_bits_equal(host(a), host(b), "same input on two streams")
+
+
+# ---- forward NTT with the automorphism folded in -------------------------------------
+
+def _galois_set(n):
+    two_n = 2 * n
+    return sorted({g % two_n for g in (1, 3, 5, 25, 2 * n - 1, n + 1, 5 ** 7)} | {1})
+
+
+@pytest.mark.parametrize("logn", list(range(1, 17)))
+def test_ntt_forward_galois_sweep(B, logn):
+    import torch
+    n = 1 << logn
+    ps = _prime_set(60 if logn % 2 else 30)
+    plan = B.Plan(n, ps, 0)
+    x = residues((2 if logn < 15 else 1, 3, n), ps, 7700 + logn)
+    tx = dev(x)
+    out = torch.empty_like(tx)
+    for g in _galois_set(n):
+        if g % 2 == 0:
+            continue
+        announce("ntt_forward_galois", logn, g)
+        B.ntt_forward_galois(plan, out, tx, g)
+        want = orc.batch_ntt(orc.batch_automorph(x, g, 0, ps), ps)
+        assert_bits_equal(host(out), want, f"NTT(sigma_{g}) n=2^{logn}")
+
+
+@pytest.mark.parametrize("w", [workloads.CHAIN, workloads.RING], ids=lambda w: w.name)
+def test_ntt_forward_galois_workload_in_place(B, w):
+    ps = primes(w.bits, 2 * w.n, w.limbs)
+    x = residues((1, 2, w.limbs, w.n), ps, w.seed_a)
+    plan = B.Plan(w.n, ps, 0)
+    for g in w.galois or workloads.galois_powers(w.n):
+        tx = dev(x)
+        announce("ntt_forward_galois in place", w.name, g)
+        B.ntt_forward_galois(plan, tx, tx, g)
+        want = orc.batch_automorph(orc.batch_ntt(x, ps), g, 1, ps)  # NTT-domain permutation of NTT(x)
+        assert_bits_equal(host(tx), want, f"{w.name} g={g}")
