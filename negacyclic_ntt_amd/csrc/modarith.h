@@ -24,10 +24,18 @@ struct Wide {
   };
   static constexpr int kPadShift = 4;  // one pad slot per 16 elements (128 B of LDS banks)
 
-  // y * w mod q, result in [0, 2q); any y < 2^64.
+  // y * w mod q, result in [0, 2q); any y < 2^64.  Q = hi64(y w'); the remainder
+  // y w - Q q is formed mod 2^64 as y w + Q (2^64 - q): one multiply-add chain
+  // (v_mad_u64_u32 accumulates the two low products) with no borrow to propagate.
   static __device__ __forceinline__ T mul(T y, Tw t, T q) {
-    uint64_t hi = __umul64hi(y, t.wp);
-    return y * t.w - hi * q;
+    const uint64_t Q = __umul64hi(y, t.wp);
+    const uint64_t nq = 0 - q;
+    const uint32_t y0 = (uint32_t)y, y1 = (uint32_t)(y >> 32);
+    const uint32_t q0 = (uint32_t)Q, q1 = (uint32_t)(Q >> 32);
+    const uint64_t lo = (uint64_t)q0 * (uint32_t)nq + (uint64_t)y0 * (uint32_t)t.w;
+    const uint32_t hi = (uint32_t)(lo >> 32) + y0 * (uint32_t)(t.w >> 32) + y1 * (uint32_t)t.w +
+                        q0 * (uint32_t)(nq >> 32) + q1 * (uint32_t)nq;
+    return ((uint64_t)hi << 32) | (uint32_t)lo;
   }
   static __device__ __forceinline__ T load(const uint64_t* p) { return *p; }
   static __device__ __forceinline__ uint64_t widen(T x) { return x; }

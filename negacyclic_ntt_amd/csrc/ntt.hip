@@ -58,6 +58,34 @@ __device__ __forceinline__ int lpos(int pos) {
   return pos + (pos >> A::kPadShift);
 }
 
+// Work placement.  Hardware block b is dispatched to XCD b % 8 of the MI355X.  The
+// logical block lb = xcd_local_block(b) gives each XCD one contiguous range of
+// logical blocks, and logical blocks are ordered limb-major (every batch item and
+// tile of plan limb 0, then limb 1, ...), so an XCD works through a contiguous
+// group of primes and keeps their twiddle tables resident in its own 4 MB L2.
+__device__ __forceinline__ uint32_t xcd_local_block(uint32_t b, uint32_t nblocks) {
+  constexpr uint32_t kXcd = 8;
+  const uint32_t full = nblocks - nblocks % kXcd;
+  if (b >= full) return b;
+  return (b % kXcd) * (full / kXcd) + b / kXcd;
+}
+struct Place {
+  uint64_t row;   // tensor row (batch item * num_limbs + limb)
+  uint32_t limb;  // plan limb
+  uint32_t tile;  // tile within the row
+};
+__device__ __forceinline__ Place place_block(uint32_t tiles_per_row, uint64_t batch, uint32_t num_limbs,
+                                             uint32_t limb_begin) {
+  const uint32_t lb = xcd_local_block(blockIdx.x, gridDim.x);
+  const uint64_t t = lb / tiles_per_row;
+  const uint32_t limb = (uint32_t)(t / batch);
+  Place pl;
+  pl.tile = lb % tiles_per_row;
+  pl.row = (t % batch) * num_limbs + limb;
+  pl.limb = limb_begin + limb;
+  return pl;
+}
+
 // Per-sub-transform parameters seen by the pass executor.
 template <class A>
 struct SubParams {
@@ -190,7 +218,10 @@ __global__ __launch_bounds__(LdsCfg<LOGN>::NT) void ntt_lds_kernel(uint64_t* dat
   constexpr int STRIDE = sub_stride<A>(LOGN);
   __shared__ T lds[ROWS * STRIDE];
   const int tid = threadIdx.x;
-  const uint64_t row0 = (uint64_t)blockIdx.x * ROWS;
+  // One row per workgroup: place limb-major across XCDs (see place_block).  Several
+  // short rows per workgroup: consecutive rows, so that loads stay coalesced.
+  uint64_t row0 = (uint64_t)blockIdx.x * ROWS;
+  if (ROWS == 1) row0 = place_block(1, total_rows / num_limbs, num_limbs, 0).row;
 
   // Coalesced load, two residues per thread per step.
   for (int e = 2 * tid; e < ROWS * N; e += 2 * NT) {
@@ -282,7 +313,7 @@ __global__ __launch_bounds__(ColCfg<LOGN1>::NT) void ntt_col_kernel(uint64_t* da
                                                                     const void* __restrict__ tw_all,
                                                                     const ModInfo* __restrict__ mods,
                                                                     uint32_t num_limbs, uint32_t limb_begin,
-                                                                    uint32_t galois_inv) {
+                                                                    uint64_t batch, uint32_t galois_inv) {
   using T = typename A::T;
   constexpr int N1 = 1 << LOGN1, N2 = 1 << LOGN2, N = N1 * N2;
   constexpr int NT = ColCfg<LOGN1>::NT;
@@ -290,9 +321,10 @@ __global__ __launch_bounds__(ColCfg<LOGN1>::NT) void ntt_col_kernel(uint64_t* da
   constexpr int BLOCKS_PER_LIMB = N2 / kCols;
   __shared__ T lds[kCols * STRIDE];
   const int tid = threadIdx.x;
-  const uint64_t row = blockIdx.x / BLOCKS_PER_LIMB;
-  const int c0 = (blockIdx.x % BLOCKS_PER_LIMB) * kCols;
-  const uint32_t limb = limb_begin + (uint32_t)(row % num_limbs);
+  const Place pl = place_block(BLOCKS_PER_LIMB, batch, num_limbs, limb_begin);
+  const uint64_t row = pl.row;
+  const int c0 = (int)pl.tile * kCols;
+  const uint32_t limb = pl.limb;
   uint64_t* base = data + row * N + c0;
   const uint64_t* src = in + row * N + c0;
 
@@ -334,7 +366,7 @@ __global__ __launch_bounds__(RowCfg<LOGN2>::NT) void ntt_row_kernel(uint64_t* __
                                                                     const void* __restrict__ tw_all,
                                                                     const ModInfo* __restrict__ mods,
                                                                     uint32_t num_limbs, uint32_t limb_begin,
-                                                                    uint32_t galois) {
+                                                                    uint64_t batch, uint32_t galois) {
   using T = typename A::T;
   constexpr int N1 = 1 << LOGN1, N2 = 1 << LOGN2, N = N1 * N2;
   constexpr int NT = RowCfg<LOGN2>::NT;
@@ -342,9 +374,10 @@ __global__ __launch_bounds__(RowCfg<LOGN2>::NT) void ntt_row_kernel(uint64_t* __
   constexpr int BLOCKS_PER_LIMB = N1 / kRows;
   __shared__ T lds[kRows * STRIDE];
   const int tid = threadIdx.x;
-  const uint64_t row = blockIdx.x / BLOCKS_PER_LIMB;
-  const int r0 = (blockIdx.x % BLOCKS_PER_LIMB) * kRows;
-  const uint32_t limb = limb_begin + (uint32_t)(row % num_limbs);
+  const Place pl = place_block(BLOCKS_PER_LIMB, batch, num_limbs, limb_begin);
+  const uint64_t row = pl.row;
+  const int r0 = (int)pl.tile * kRows;
+  const uint32_t limb = pl.limb;
   uint64_t* base = data + row * N + (size_t)r0 * N2;
 
   for (int e = 2 * tid; e < kRows * N2; e += 2 * NT) {
@@ -421,25 +454,26 @@ template <class A, int LOGN1, int LOGN2>
 hipError_t launch_split(const ntt_plan* p, uint64_t* data, const uint64_t* in, uint64_t rows, uint32_t limb_begin,
                         uint32_t num_limbs, Op op, uint32_t g, hipStream_t s) {
   const void* tw = tables_for<A>(p, op);
+  const uint64_t batch = rows / num_limbs;
   const dim3 col_grid((uint32_t)(rows * ((1u << LOGN2) / kCols))), col_block(ColCfg<LOGN1>::NT);
   const dim3 row_grid((uint32_t)(rows * ((1u << LOGN1) / kRows))), row_block(RowCfg<LOGN2>::NT);
   if (op == Op::kForward) {
     hipLaunchKernelGGL((ntt_col_kernel<A, LOGN1, LOGN2, true, false, false>), col_grid, col_block, 0, s, data, in,
-                       tw, p->d_mods, num_limbs, limb_begin, 1u);
+                       tw, p->d_mods, num_limbs, limb_begin, batch, 1u);
     hipLaunchKernelGGL((ntt_row_kernel<A, LOGN1, LOGN2, true, true, false>), row_grid, row_block, 0, s, data, tw,
-                       p->d_mods, num_limbs, limb_begin, 1u);
+                       p->d_mods, num_limbs, limb_begin, batch, 1u);
   } else if (op == Op::kForwardGalois) {
     const uint32_t two_n = 2u << (LOGN1 + LOGN2);
     const uint32_t h = (uint32_t)host_invmod(g % two_n, two_n);
     hipLaunchKernelGGL((ntt_col_kernel<A, LOGN1, LOGN2, true, false, true>), col_grid, col_block, 0, s, data, in,
-                       tw, p->d_mods, num_limbs, limb_begin, h);
+                       tw, p->d_mods, num_limbs, limb_begin, batch, h);
     hipLaunchKernelGGL((ntt_row_kernel<A, LOGN1, LOGN2, true, true, true>), row_grid, row_block, 0, s, data, tw,
-                       p->d_mods, num_limbs, limb_begin, g);
+                       p->d_mods, num_limbs, limb_begin, batch, g);
   } else {
     hipLaunchKernelGGL((ntt_row_kernel<A, LOGN1, LOGN2, false, false, false>), row_grid, row_block, 0, s, data, tw,
-                       p->d_mods, num_limbs, limb_begin, 1u);
+                       p->d_mods, num_limbs, limb_begin, batch, 1u);
     hipLaunchKernelGGL((ntt_col_kernel<A, LOGN1, LOGN2, false, true, false>), col_grid, col_block, 0, s, data, data,
-                       tw, p->d_mods, num_limbs, limb_begin, 1u);
+                       tw, p->d_mods, num_limbs, limb_begin, batch, 1u);
   }
   return hipGetLastError();
 }
