@@ -27,6 +27,42 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+# Integer ALU peak: 256 CUs x 64 lanes x 2.4 GHz of full-rate 32-bit multiply issue
+# (v_mul_lo_u32 / v_mul_hi_u32 / v_mad_u64_u32 all issue at full rate on gfx950).
+MUL32_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
+# A lazy 64-bit Shoup butterfly needs at least 10 32x32-bit multiplies: 4 for the
+# high half of y * w', 3 for the low half of y * w, 3 for the low half of Q * q.
+MUL32_PER_BUTTERFLY = 10
+CALIBRATION_COPY_BYTES = 256 << 20
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_sources_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("modarith.h", "ntt.hip"):
+        with open(os.path.join(ROOT, "negacyclic_ntt_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per forward-NTT call from the committed counter summary, if it was
+    taken on the current kernel sources (else None)."""
+    path = os.path.join(PROFILES, "ntt_forward_n65536_q24x60_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if line.startswith("- ") and ":" in line:
+            k, v = line[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel_sources_sha256_16") != kernel_sources_digest():
+        return None
+    try:
+        return int(fields["hbm_bytes_per_call"])
+    except (KeyError, ValueError):
+        return None
 
 
 def parse():
@@ -36,8 +72,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--rotate", type=int, default=3, help="distinct input sets cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-limbs", type=int, default=48,
-                    help="limbs of the batch the oracle processes for the CPU baseline")
+    ap.add_argument("--cpu-sample-limbs", type=int, default=384,
+                    help="limbs of the batch the oracle processes for the CPU baseline (384 = all 16 polys)")
     return ap.parse_args()
 
 
@@ -48,7 +84,7 @@ def cpu_baseline(primes, n, nq, npr, dnum, sample_limbs, a_host, b_host, ct_host
     import oracle as orc
     threads = orc.default_threads()
     L = nq
-    rows = max(1, sample_limbs // L)  # whole polynomials of the batch
+    rows = max(2, min(a_host.size // (L * n), sample_limbs // L))  # whole polynomials of the batch
     a = np.ascontiguousarray(a_host.reshape(-1, L, n)[:rows])
     b = np.ascontiguousarray(b_host.reshape(-1, L, n)[:rows])
     qs = primes[:L]
@@ -113,6 +149,12 @@ def main():
         ws = B.workspace(ksp, 1)
     except B.NttError:
         ksp = None
+    # A plain device copy of known size: its FETCH_SIZE / WRITE_SIZE counters
+    # calibrate the HBM byte counters of the other kernels.
+    cal_src = torch.empty(CALIBRATION_COPY_BYTES // 8, dtype=torch.int64, device=dev).fill_(1)
+    cal_dst = torch.empty_like(cal_src)
+    cal_dst.copy_(cal_src)
+    del cal_src, cal_dst
     torch.cuda.synchronize()
     gen_s = time.perf_counter() - t_gen
     resident_bytes = sum(t.numel() * 8 for pair in sets for t in pair) + sum(k.numel() * 8 for k in keys)
@@ -179,16 +221,25 @@ def main():
     if "keyswitch" in mean_ms:
         per_row["keyswitch"]["keyswitch_per_s"] = round(1e3 / mean_ms["keyswitch"], 1)
 
-    dom = max(mean_ms, key=mean_ms.get)
-    dom_gbps = alg_bytes[dom] / (mean_ms[dom] * 1e-3) / 1e9
+    # Dominant operation: the forward NTT (two launches: column pass + row pass).
+    # Its algorithmic work per call: limb * (n/2) log2(n) butterflies, 16 n bytes per limb.
+    fwd_s = mean_ms["ntt_forward"] * 1e-3
+    butterflies = limb * (n // 2) * (n.bit_length() - 1)
+    alu_tops = butterflies * MUL32_PER_BUTTERFLY / fwd_s / 1e12
+    fwd_gbps = alg_bytes["ntt_forward"] / fwd_s / 1e9
+    traffic = recorded_traffic()
     roofline = {
-        "kernel": dom,
-        "bound": "hbm",
-        "achieved": round(dom_gbps, 1),
-        "peak": HBM_PEAK_GBPS,
-        "unit": "GB/s",
-        "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
-        "traffic": None,
+        "kernel": "ntt_forward (ntt_col_kernel + ntt_row_kernel, n=2^16, 384 limbs)",
+        "bound": "alu",
+        "achieved": round(alu_tops, 3),
+        "peak": round(MUL32_PEAK_TOPS, 2),
+        "unit": "TOP/s",
+        "frac": round(alu_tops / MUL32_PEAK_TOPS, 4),
+        "traffic": traffic,
+        "ops": "32-bit multiplies, 10 per 64-bit Shoup butterfly",
+        "hbm_alg_GBps": round(fwd_gbps, 1),
+        "hbm_frac": round(fwd_gbps / HBM_PEAK_GBPS, 4),
+        "us_per_call": round(fwd_s * 1e6, 2),
     }
     rt_ms = mean_ms["ntt_forward"] + mean_ms["ntt_inverse"]
     out = {

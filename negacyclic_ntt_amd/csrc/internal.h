@@ -15,6 +15,7 @@ namespace nntt {
 struct ModInfo {
   uint64_t q;
   uint64_t n_inv, n_inv_shoup;  // n^-1 mod q and floor(n^-1 * 2^64 / q)
+  uint64_t n_inv_shoup60;       // floor(n^-1 * 2^62 / q) (primes below 2^60)
   uint32_t n_inv32, n_inv_shoup32;  // narrow (q < 2^30) Shoup pair, else 0
   Barrett br;
 };
@@ -29,11 +30,14 @@ struct ntt_plan {
   int device = -1;
   std::vector<uint64_t> primes, psis;
   std::vector<uint8_t> narrow;                   // 1 if q < 2^30
+  std::vector<uint8_t> below60;                  // 1 if q < 2^60
   std::vector<uint64_t> h_fwd, h_fwd_sh, h_inv, h_inv_sh;  // host tables [L][n]
   std::vector<nntt::ModInfo> h_mods;
   // device copies
   nntt::Wide::Tw* d_fwd = nullptr;    // [L][n] {psi^brv(k), shoup}
   nntt::Wide::Tw* d_inv = nullptr;    // [L][n] {psi^-brv(k), shoup}
+  nntt::Wide60::Tw* d_fwd60 = nullptr;  // [L][n] {w, floor(w * 2^62 / q)}, zero for q >= 2^60
+  nntt::Wide60::Tw* d_inv60 = nullptr;
   nntt::Narrow::Tw* d_fwd32 = nullptr;  // [L][n], entries of wide primes are zero
   nntt::Narrow::Tw* d_inv32 = nullptr;
   nntt::ModInfo* d_mods = nullptr;    // [L]
@@ -63,6 +67,8 @@ hipError_t launch_ntt_galois(const ntt_plan* p, uint64_t* out, const uint64_t* i
                              uint32_t limb_begin, uint32_t num_limbs, hipStream_t s);
 // True when every prime in [limb_begin, limb_begin + num_limbs) is below 2^30.
 bool range_is_narrow(const ntt_plan* p, uint32_t limb_begin, uint32_t num_limbs);
+// True when every prime in the range is below 2^60.
+bool range_below60(const ntt_plan* p, uint32_t limb_begin, uint32_t num_limbs);
 
 // Element-wise launchers (elementwise.hip).
 hipError_t launch_pointwise(const ntt_plan* p, uint64_t* out, const uint64_t* a, const uint64_t* b, uint64_t batch,

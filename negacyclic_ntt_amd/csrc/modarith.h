@@ -23,6 +23,8 @@ struct Wide {
     uint64_t w, wp;
   };
   static constexpr int kPadShift = 4;  // one pad slot per 16 elements (128 B of LDS banks)
+  static constexpr bool kSignSelect = false;  // values reach 4q < 2^64: full unsigned compare
+  static constexpr int kShoupBits = 64;
 
   // y * w mod q, result in [0, 2q); any y < 2^64.  Q = hi64(y w'); the remainder
   // y w - Q q is formed mod 2^64 as y w + Q (2^64 - q): one multiply-add chain
@@ -41,12 +43,47 @@ struct Wide {
   static __device__ __forceinline__ uint64_t widen(T x) { return x; }
 };
 
+// q < 2^60: values stay below 4q < 2^62, which allows a Shoup constant scaled by
+// 2^62, w' = floor(w * 2^62 / q) < 2^62.  Then with y = y1 2^32 + y0 (y1 < 2^30)
+// and w' = p1 2^32 + p0 (p1 < 2^30) the middle sum
+//   S = y0 p1 + y1 p0 + hi32(y0 p0) < 2^64
+// cannot overflow, and Q = floor(y w' / 2^62) = (y1 p1 2^32 + S) >> 30 (the low
+// 32 bits of y0 p0 never change the quotient).  Q >= floor(y w / q) - 1, so the
+// remainder stays in [0, 2q).  No carries to track, fewer register-pair moves.
+struct Wide60 {
+  using T = uint64_t;
+  struct Tw {
+    uint64_t w, wp;
+  };
+  static constexpr int kPadShift = 4;
+  static constexpr bool kSignSelect = true;  // values < 4q < 2^62
+  static constexpr int kShoupBits = 62;
+
+  static __device__ __forceinline__ T mul(T y, Tw t, T q) {
+    const uint32_t y0 = (uint32_t)y, y1 = (uint32_t)(y >> 32);
+    const uint32_t p0 = (uint32_t)t.wp, p1 = (uint32_t)(t.wp >> 32);
+    uint64_t S = (uint64_t)y0 * p1 + __umulhi(y0, p0);
+    S = (uint64_t)y1 * p0 + S;
+    const uint64_t H = (uint64_t)y1 * p1 + (S >> 32);
+    const uint64_t Q = (H << 2) | ((uint32_t)S >> 30);
+    const uint64_t nq = 0 - q;
+    const uint32_t q0 = (uint32_t)Q, q1 = (uint32_t)(Q >> 32);
+    const uint64_t lo = (uint64_t)q0 * (uint32_t)nq + (uint64_t)y0 * (uint32_t)t.w;
+    const uint32_t hi = (uint32_t)(lo >> 32) + y0 * (uint32_t)(t.w >> 32) + y1 * (uint32_t)t.w +
+                        q0 * (uint32_t)(nq >> 32) + q1 * (uint32_t)nq;
+    return ((uint64_t)hi << 32) | (uint32_t)lo;
+  }
+  static __device__ __forceinline__ uint64_t widen(T x) { return x; }
+};
+
 struct Narrow {
   using T = uint32_t;
   struct Tw {
     uint32_t w, wp;
   };
   static constexpr int kPadShift = 5;  // one pad slot per 32 elements
+  static constexpr bool kSignSelect = false;
+  static constexpr int kShoupBits = 32;
 
   static __device__ __forceinline__ T mul(T y, Tw t, T q) {
     uint32_t hi = __umulhi(y, t.wp);
@@ -61,13 +98,36 @@ __device__ __forceinline__ T csub(T x, T m) {
   return x >= m ? x - m : x;
 }
 
+// The same for x < 2^63 and m <= 2^62 without compare/carry (no VCC hazards):
+// d = x - m is negative exactly when x < m; keep x there, else d.  The select is a
+// bit-field insert on the sign mask.
+__device__ __forceinline__ uint64_t csub_sign(uint64_t x, uint64_t m) {
+  // x + (2^64 - m): a single 64-bit add (v_lshl_add_u64).  The empty asm keeps the
+  // optimiser from folding the negation back into a borrow-chain subtraction.
+  uint64_t nm = 0 - m;
+  asm("" : "+v"(nm));
+  const uint64_t d = x + nm;
+  const uint32_t mask = (uint32_t)((int32_t)(uint32_t)(d >> 32) >> 31);
+  uint32_t lo, hi;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(lo) : "v"(mask), "v"((uint32_t)x), "v"((uint32_t)d));
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(hi) : "v"(mask), "v"((uint32_t)(x >> 32)), "v"((uint32_t)(d >> 32)));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Lazy reduction used by the butterflies (per residue width).
+template <class A>
+__device__ __forceinline__ typename A::T reduce_once(typename A::T x, typename A::T m) {
+  if constexpr (sizeof(typename A::T) == 8 && A::kSignSelect) return csub_sign(x, m);
+  else return csub(x, m);
+}
+
 // Cooley-Tukey (decimation in time) butterfly with lazy reduction.
 // In: x, y in [0, 4q).  Out: x + w y, x - w y + 2q, both in [0, 4q).
 template <class A>
 __device__ __forceinline__ void ct_butterfly(typename A::T& x, typename A::T& y, typename A::Tw w, typename A::T q,
                                              typename A::T two_q) {
   using T = typename A::T;
-  T u = csub(x, two_q);
+  T u = reduce_once<A>(x, two_q);
   T t = A::mul(y, w, q);
   x = u + t;
   y = u - t + two_q;
@@ -81,7 +141,7 @@ __device__ __forceinline__ void gs_butterfly(typename A::T& x, typename A::T& y,
   using T = typename A::T;
   T s = x + y;
   T d = x - y + two_q;
-  x = csub(s, two_q);
+  x = reduce_once<A>(s, two_q);
   y = A::mul(d, w, q);
 }
 

@@ -30,15 +30,28 @@
 namespace nntt {
 namespace {
 
-// Split m stages into passes of at most 4 (radix 16), as even as possible.
+// Register radix (log2) of one pass, and the column / row tile of the two-pass
+// split.  Compile-time tuning knobs; the defaults are the measured best on gfx950.
+#ifndef NNTT_MAX_RADIX_LOG
+#define NNTT_MAX_RADIX_LOG 4
+#endif
+#ifndef NNTT_COL_TILE
+#define NNTT_COL_TILE 16
+#endif
+#ifndef NNTT_ROW_TILE
+#define NNTT_ROW_TILE 16
+#endif
+constexpr int kMaxRadixLog = NNTT_MAX_RADIX_LOG;
+
+// Split m stages into passes of at most kMaxRadixLog, as even as possible.
 struct Sched {
   int np;
-  int r[5];
-  int s[5];
+  int r[8];
+  int s[8];
 };
 constexpr Sched make_sched(int logm) {
   Sched S{};
-  S.np = logm <= 4 ? 1 : (logm + 3) / 4;
+  S.np = logm <= kMaxRadixLog ? 1 : (logm + kMaxRadixLog - 1) / kMaxRadixLog;
   int base = logm / S.np, extra = logm % S.np, s = 0;
   for (int i = 0; i < S.np; ++i) {
     S.r[i] = base + (i < extra ? 1 : 0);
@@ -180,9 +193,12 @@ __device__ __forceinline__ uint64_t finish(typename A::T x, const ModInfo& m) {
     return A::widen(csub<T>(x, q));
   }
   typename A::Tw s;
-  if constexpr (sizeof(T) == 8) {
+  if constexpr (A::kShoupBits == 64) {
     s.w = m.n_inv;
     s.wp = m.n_inv_shoup;
+  } else if constexpr (A::kShoupBits == 62) {
+    s.w = m.n_inv;
+    s.wp = m.n_inv_shoup60;
   } else {
     s.w = m.n_inv32;
     s.wp = m.n_inv_shoup32;
@@ -197,8 +213,9 @@ struct LdsCfg {
   static constexpr Sched S = make_sched(LOGN);
   static constexpr int RMAX = S.r[0];
   static constexpr int N = 1 << LOGN;
-  static constexpr int NT = (N >> RMAX) >= 256 ? (N >> RMAX) : 256;
-  static constexpr int ROWS = (NT << RMAX) / N;
+  static constexpr int NT0 = (N >> RMAX) >= 256 ? (N >> RMAX) : 256;
+  static constexpr int NT = NT0 > 1024 ? 1024 : NT0;
+  static constexpr int ROWS = (NT << RMAX) / N > 0 ? (NT << RMAX) / N : 1;
 };
 
 // GAL: the coefficient-domain automorphism sigma_g is applied while loading
@@ -269,8 +286,8 @@ __global__ __launch_bounds__(LdsCfg<LOGN>::NT) void ntt_lds_kernel(uint64_t* dat
 // Two-pass split for n = N1 * N2 (N2 contiguous).  Column kernel: a workgroup
 // owns COLS adjacent columns (COLS * 8 B = one 128 B line per row) of one limb.
 // Row kernel: a workgroup owns ROWS consecutive rows of one limb.
-constexpr int kCols = 16;
-constexpr int kRows = 16;
+constexpr int kCols = NNTT_COL_TILE;
+constexpr int kRows = NNTT_ROW_TILE;
 
 template <int LOGN1>
 struct ColCfg {
@@ -427,7 +444,8 @@ enum class Op { kForward, kInverse, kForwardGalois };
 template <class A>
 const void* tables_for(const ntt_plan* p, Op op) {
   const bool inv = op == Op::kInverse;
-  if (sizeof(typename A::T) == 8) return inv ? (const void*)p->d_inv : (const void*)p->d_fwd;
+  if (A::kShoupBits == 64) return inv ? (const void*)p->d_inv : (const void*)p->d_fwd;
+  if (A::kShoupBits == 62) return inv ? (const void*)p->d_inv60 : (const void*)p->d_fwd60;
   return inv ? (const void*)p->d_inv32 : (const void*)p->d_fwd32;
 }
 
@@ -515,6 +533,8 @@ hipError_t dispatch(const ntt_plan* p, uint64_t* data, const uint64_t* in, uint6
   if (rows == 0) return hipSuccess;
   if (range_is_narrow(p, limb_begin, num_limbs))
     return launch_any<Narrow>(p, data, in, rows, limb_begin, num_limbs, op, g, s);
+  if (range_below60(p, limb_begin, num_limbs))
+    return launch_any<Wide60>(p, data, in, rows, limb_begin, num_limbs, op, g, s);
   return launch_any<Wide>(p, data, in, rows, limb_begin, num_limbs, op, g, s);
 }
 
@@ -523,6 +543,12 @@ hipError_t dispatch(const ntt_plan* p, uint64_t* data, const uint64_t* in, uint6
 bool range_is_narrow(const ntt_plan* p, uint32_t limb_begin, uint32_t num_limbs) {
   for (uint32_t l = limb_begin; l < limb_begin + num_limbs; ++l)
     if (!p->narrow[l]) return false;
+  return true;
+}
+
+bool range_below60(const ntt_plan* p, uint32_t limb_begin, uint32_t num_limbs) {
+  for (uint32_t l = limb_begin; l < limb_begin + num_limbs; ++l)
+    if (!p->below60[l]) return false;
   return true;
 }
 

@@ -146,10 +146,13 @@ static void free_device(ntt_plan* p) {
   DeviceGuard g(p->device);
   (void)hipFree(p->d_fwd);
   (void)hipFree(p->d_inv);
+  (void)hipFree(p->d_fwd60);
+  (void)hipFree(p->d_inv60);
   (void)hipFree(p->d_fwd32);
   (void)hipFree(p->d_inv32);
   (void)hipFree(p->d_mods);
   p->d_fwd = p->d_inv = nullptr;
+  p->d_fwd60 = p->d_inv60 = nullptr;
   p->d_fwd32 = p->d_inv32 = nullptr;
   p->d_mods = nullptr;
 }
@@ -193,6 +196,7 @@ extern "C" int ntt_plan_create(ntt_plan** out, uint32_t n, const uint64_t* prime
   p->primes.assign(primes, primes + num_primes);
   p->psis.resize(num_primes);
   p->narrow.resize(num_primes);
+  p->below60.resize(num_primes);
   size_t tn = (size_t)num_primes * n;
   p->h_fwd.resize(tn);
   p->h_fwd_sh.resize(tn);
@@ -200,6 +204,7 @@ extern "C" int ntt_plan_create(ntt_plan** out, uint32_t n, const uint64_t* prime
   p->h_inv_sh.resize(tn);
   p->h_mods.resize(num_primes);
   std::vector<Wide::Tw> fwd(tn), inv(tn);
+  std::vector<Wide60::Tw> fwd60(tn, Wide60::Tw{0, 0}), inv60(tn, Wide60::Tw{0, 0});
   std::vector<Narrow::Tw> fwd32(tn, Narrow::Tw{0, 0}), inv32(tn, Narrow::Tw{0, 0});
   std::vector<uint64_t> pw(n), ipw(n);
 
@@ -213,6 +218,7 @@ extern "C" int ntt_plan_create(ntt_plan** out, uint32_t n, const uint64_t* prime
     uint64_t ips = host_invmod(ps, q);
     p->psis[l] = ps;
     p->narrow[l] = q < (1ull << 30);
+    p->below60[l] = q < (1ull << 60);
     pw[0] = ipw[0] = 1;
     for (uint32_t e = 1; e < n; ++e) {
       pw[e] = host_mulmod(pw[e - 1], ps, q);
@@ -228,6 +234,10 @@ extern "C" int ntt_plan_create(ntt_plan** out, uint32_t n, const uint64_t* prime
       p->h_inv_sh[i] = iwsh;
       fwd[i] = Wide::Tw{w, wsh};
       inv[i] = Wide::Tw{iw, iwsh};
+      if (p->below60[l]) {  // floor(w 2^62 / q) = floor(floor(w 2^64 / q) / 4)
+        fwd60[i] = Wide60::Tw{w, wsh >> 2};
+        inv60[i] = Wide60::Tw{iw, iwsh >> 2};
+      }
       if (p->narrow[l]) {
         fwd32[i] = Narrow::Tw{(uint32_t)w, (uint32_t)(((uint64_t)w << 32) / q)};
         inv32[i] = Narrow::Tw{(uint32_t)iw, (uint32_t)(((uint64_t)iw << 32) / q)};
@@ -238,6 +248,7 @@ extern "C" int ntt_plan_create(ntt_plan** out, uint32_t n, const uint64_t* prime
     m.q = q;
     m.n_inv = host_invmod(n % q, q);
     m.n_inv_shoup = (uint64_t)(((u128)m.n_inv << 64) / q);
+    m.n_inv_shoup60 = p->below60[l] ? (uint64_t)(((u128)m.n_inv << 62) / q) : 0;
     if (p->narrow[l]) {
       m.n_inv32 = (uint32_t)m.n_inv;
       m.n_inv_shoup32 = (uint32_t)(((uint64_t)m.n_inv << 32) / q);
@@ -250,6 +261,8 @@ extern "C" int ntt_plan_create(ntt_plan** out, uint32_t n, const uint64_t* prime
     int rc = g.ok ? NTT_OK : NTT_EDEVICE;
     if (rc == NTT_OK) rc = upload(&p->d_fwd, fwd.data(), tn * sizeof(Wide::Tw));
     if (rc == NTT_OK) rc = upload(&p->d_inv, inv.data(), tn * sizeof(Wide::Tw));
+    if (rc == NTT_OK) rc = upload(&p->d_fwd60, fwd60.data(), tn * sizeof(Wide60::Tw));
+    if (rc == NTT_OK) rc = upload(&p->d_inv60, inv60.data(), tn * sizeof(Wide60::Tw));
     if (rc == NTT_OK) rc = upload(&p->d_fwd32, fwd32.data(), tn * sizeof(Narrow::Tw));
     if (rc == NTT_OK) rc = upload(&p->d_inv32, inv32.data(), tn * sizeof(Narrow::Tw));
     if (rc == NTT_OK) rc = upload(&p->d_mods, p->h_mods.data(), num_primes * sizeof(ModInfo));
