@@ -13,6 +13,16 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Streaming 16-byte accesses: every residue is touched once, so loads and stores are
+// marked non-temporal (they bypass reuse-oriented cache allocation).
+typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u64x2 ld_stream(const uint64_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u64x2*>(p));
+}
+__device__ __forceinline__ void st_stream(uint64_t* p, u64x2 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u64x2*>(p));
+}
+
 // Blocks are dispatched round-robin over the 8 XCDs of an MI355X; this maps the
 // hardware block id to a logical id so that each XCD works on one contiguous
 // range of logical blocks (and hence of the tensor), keeping its L2 working set
@@ -34,12 +44,12 @@ __global__ __launch_bounds__(kThreads) void pointwise_kernel(uint64_t* __restric
   if (p >= pairs) return;
   const uint64_t e = 2 * p;
   const Barrett br = mods[limb_begin + (uint32_t)((e >> logn) % num_limbs)].br;
-  const ulonglong2 x = *reinterpret_cast<const ulonglong2*>(a + e);
-  const ulonglong2 y = *reinterpret_cast<const ulonglong2*>(b + e);
-  ulonglong2 z;
+  const u64x2 x = ld_stream(a + e);
+  const u64x2 y = ld_stream(b + e);
+  u64x2 z;
   z.x = barrett_mul(x.x, y.x, br);
   z.y = barrett_mul(x.y, y.y, br);
-  *reinterpret_cast<ulonglong2*>(out + e) = z;
+  st_stream(out + e, z);
 }
 
 // a, b: [batch][2][L][n]; out: [batch][3][L][n].
@@ -59,20 +69,20 @@ __global__ __launch_bounds__(kThreads) void tensor_kernel(uint64_t* __restrict__
   const uint64_t* a0 = a + bi * 2 * plane + off;
   const uint64_t* b0 = b + bi * 2 * plane + off;
   uint64_t* d0 = out + bi * 3 * plane + off;
-  const ulonglong2 x0 = *reinterpret_cast<const ulonglong2*>(a0);
-  const ulonglong2 x1 = *reinterpret_cast<const ulonglong2*>(a0 + plane);
-  const ulonglong2 y0 = *reinterpret_cast<const ulonglong2*>(b0);
-  const ulonglong2 y1 = *reinterpret_cast<const ulonglong2*>(b0 + plane);
-  ulonglong2 r0, r1, r2;
+  const u64x2 x0 = ld_stream(a0);
+  const u64x2 x1 = ld_stream(a0 + plane);
+  const u64x2 y0 = ld_stream(b0);
+  const u64x2 y1 = ld_stream(b0 + plane);
+  u64x2 r0, r1, r2;
   r0.x = barrett_mul(x0.x, y0.x, br);
   r0.y = barrett_mul(x0.y, y0.y, br);
   r1.x = add_mod(barrett_mul(x0.x, y1.x, br), barrett_mul(x1.x, y0.x, br), q);
   r1.y = add_mod(barrett_mul(x0.y, y1.y, br), barrett_mul(x1.y, y0.y, br), q);
   r2.x = barrett_mul(x1.x, y1.x, br);
   r2.y = barrett_mul(x1.y, y1.y, br);
-  *reinterpret_cast<ulonglong2*>(d0) = r0;
-  *reinterpret_cast<ulonglong2*>(d0 + plane) = r1;
-  *reinterpret_cast<ulonglong2*>(d0 + 2 * plane) = r2;
+  st_stream(d0, r0);
+  st_stream(d0 + plane, r1);
+  st_stream(d0 + 2 * plane, r2);
 }
 
 // Coefficient domain: out[e] = in[i] if i < n else -in[i - n], i = e * h mod 2n,
@@ -98,7 +108,7 @@ __global__ __launch_bounds__(kThreads) void automorph_coeff_kernel(uint64_t* __r
     v = src[i];
   else
     v = neg_mod(src[i - n], q);
-  out[idx] = v;
+  __builtin_nontemporal_store(v, out + idx);
 }
 
 // NTT domain (bit-reversed slots): out[k] = in[p(k)], 2 brv(p) + 1 = (2 brv(k) + 1) g mod 2n.

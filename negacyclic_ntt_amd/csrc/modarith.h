@@ -69,8 +69,8 @@ struct Wide60 {
     const uint64_t nq = 0 - q;
     const uint32_t q0 = (uint32_t)Q, q1 = (uint32_t)(Q >> 32);
     const uint64_t lo = (uint64_t)q0 * (uint32_t)nq + (uint64_t)y0 * (uint32_t)t.w;
-    const uint32_t hi = (uint32_t)(lo >> 32) + y0 * (uint32_t)(t.w >> 32) + y1 * (uint32_t)t.w +
-                        q0 * (uint32_t)(nq >> 32) + q1 * (uint32_t)nq;
+    const uint32_t hi = (uint32_t)(lo >> 32) + y0 * (uint32_t)(t.w >> 32) + y1 * (uint32_t)t.w + q0 * (uint32_t)(nq >> 32) +
+                        q1 * (uint32_t)nq;
     return ((uint64_t)hi << 32) | (uint32_t)lo;
   }
   static __device__ __forceinline__ uint64_t widen(T x) { return x; }

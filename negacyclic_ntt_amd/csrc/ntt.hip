@@ -130,9 +130,9 @@ __device__ __forceinline__ void run_pass(typename A::T* lds, int tid, const GetS
     const T q = sp.q, two_q = q + q;
     const uint32_t pg = (sp.prefix << S0) + (uint32_t)g;
     T x[1 << R];
-#pragma unroll
-    for (int i = 0; i < (1 << R); ++i) x[i] = base[lpos<A>(pos0 + i * TP)];
     if (FWD) {
+#pragma unroll
+      for (int i = 0; i < (1 << R); ++i) x[i] = base[lpos<A>(pos0 + i * TP)];
 #pragma unroll
       for (int v = 0; v < R; ++v) {
         const int half = 1 << (R - 1 - v);
@@ -144,14 +144,24 @@ __device__ __forceinline__ void run_pass(typename A::T* lds, int tid, const GetS
         }
       }
     } else {
+      // The inverse network needs its largest group of twiddles first: request all
+      // 2^R - 1 of the set before the LDS reads so that their latency overlaps.
+      // wv[(1 << v) - 1 + j] = stage v, group j.  (Measured: -4% on the inverse,
+      // while the same preload slows the forward network, which starts with one.)
+      typename A::Tw wv[(1 << R) - 1];
+#pragma unroll
+      for (int v = 0; v < R; ++v)
+#pragma unroll
+        for (int j = 0; j < (1 << v); ++j) wv[(1 << v) - 1 + j] = sp.tw[(pg << v) + (uint32_t)j];
+#pragma unroll
+      for (int i = 0; i < (1 << R); ++i) x[i] = base[lpos<A>(pos0 + i * TP)];
 #pragma unroll
       for (int v = R - 1; v >= 0; --v) {
         const int half = 1 << (R - 1 - v);
 #pragma unroll
         for (int i = 0; i < (1 << R); ++i) {
           if (i & half) continue;
-          const typename A::Tw w = sp.tw[(pg << v) + (uint32_t)(i >> (R - v))];
-          gs_butterfly<A>(x[i], x[i + half], w, q, two_q);
+          gs_butterfly<A>(x[i], x[i + half], wv[(1 << v) - 1 + (i >> (R - v))], q, two_q);
         }
       }
     }
