@@ -32,22 +32,41 @@ namespace nntt {
 namespace {
 
 constexpr int kKsThreads = 256;
+#ifndef NNTT_MODUP_GROUPS
+#define NNTT_MODUP_GROUPS 2
+#endif
+#ifndef NNTT_MODDOWN_GROUPS
+#define NNTT_MODDOWN_GROUPS 2
+#endif
+constexpr uint32_t kModUpGroups = NNTT_MODUP_GROUPS;
+constexpr uint32_t kModDownGroups = NNTT_MODDOWN_GROUPS;
 constexpr int kMaxDigitPrimes = 16;  // table row strides of the device constants
 constexpr int kMaxSpecial = 16;
 
 using Tw = Wide::Tw;
 
-__device__ __forceinline__ uint64_t shoup(uint64_t y, Tw c, uint64_t q) { return Wide::mul(y, c, q); }
+// Shoup product by a plan constant {w, floor(w 2^64 / q)}.  When every prime of the
+// plan is below 2^60 (B60), the 2^62-scaled companion floor(floor(w 2^64/q) / 4) is
+// used with the cheaper carry-free quotient (see Wide60); the shift is on a uniform
+// constant, so it runs on the scalar unit.
+template <bool B60>
+__device__ __forceinline__ uint64_t shoup(uint64_t y, Tw c, uint64_t q) {
+  if constexpr (B60) return Wide60::mul(y, Wide60::Tw{c.w, c.wp >> 2}, q);
+  else return Wide::mul(y, c, q);
+}
 
-// acc, t in [0, 2q) -> (acc + t) in [0, 2q)
+// acc, t in [0, 2q) -> (acc + t) in [0, 2q).  Below 2^60 the sum stays below 2^62,
+// so the compare-free sign select applies.
+template <bool B60>
 __device__ __forceinline__ uint64_t lazy_add(uint64_t acc, uint64_t t, uint64_t two_q) {
-  return csub(acc + t, two_q);
+  if constexpr (B60) return csub_sign(acc + t, two_q);
+  else return csub(acc + t, two_q);
 }
 
 // Garner digits of k residues (k <= K, runtime).  m[i] the moduli, g[i * S + k]
 // (S = table row stride) holds prod_{j<k} m_j mod m_i for k < i and
 // (prod_{j<i} m_j)^-1 mod m_i at k = i.  Output v[i] canonical mod m[i].
-template <int K, int S>
+template <bool B60, int K, int S>
 __device__ __forceinline__ void garner(const uint64_t (&x)[K], uint64_t (&v)[K], uint32_t k,
                                        const uint64_t* __restrict__ m, const Tw* __restrict__ g) {
   static_assert(K <= S, "register width exceeds the table stride");
@@ -57,15 +76,15 @@ __device__ __forceinline__ void garner(const uint64_t (&x)[K], uint64_t (&v)[K],
     const uint64_t mi = m[i], two = mi + mi;
     uint64_t s = 0;
 #pragma unroll
-    for (int kk = 0; kk < i; ++kk) s = lazy_add(s, shoup(v[kk], g[i * S + kk], mi), two);
+    for (int kk = 0; kk < i; ++kk) s = lazy_add<B60>(s, shoup<B60>(v[kk], g[i * S + kk], mi), two);
     // x_i - s + 2 m_i in (0, 3 m_i)
     const uint64_t y = x[i] + two - s;
-    v[i] = csub(i == 0 ? x[0] : shoup(y, g[i * S + i], mi), mi);
+    v[i] = csub(i == 0 ? x[0] : shoup<B60>(y, g[i * S + i], mi), mi);
   }
 }
 
 // sum_i v_i c_i mod p, canonical.  c[i] = prod_{j<i} m_j mod p (Shoup pairs).
-template <int K>
+template <bool B60, int K>
 __device__ __forceinline__ uint64_t mixed_radix_eval(const uint64_t (&v)[K], uint32_t k, const Tw* __restrict__ c,
                                                      uint64_t p) {
   const uint64_t two = p + p;
@@ -73,7 +92,7 @@ __device__ __forceinline__ uint64_t mixed_radix_eval(const uint64_t (&v)[K], uin
 #pragma unroll
   for (int i = 0; i < K; ++i) {
     if (i >= (int)k) break;
-    s = lazy_add(s, shoup(v[i], c[i], p), two);
+    s = lazy_add<B60>(s, shoup<B60>(v[i], c[i], p), two);
   }
   return csub(s, p);
 }
@@ -101,8 +120,12 @@ struct KsDev {
 };
 
 // ---- ModUp with the automorphism fused on load ---------------------------------
-// grid.x: coefficient tiles; grid.y: batch * dnum.  ext: [batch][dnum][nq+np][n].
-template <int K>
+// grid.x: coefficient tiles; grid.y: batch * dnum; grid.z: groups of target primes.
+// Each thread lifts one coefficient of one digit (Garner) and reduces it onto its
+// group's share of the nq + np - alpha other primes: the groups multiply the
+// number of resident waves (the Garner digits are recomputed per group).
+// ext: [batch][dnum][nq+np][n].
+template <bool B60, int K>
 __global__ __launch_bounds__(kKsThreads) void modup_kernel(uint64_t* __restrict__ ext,
                                                            const uint64_t* __restrict__ ct, KsDev kc, uint32_t logn,
                                                            uint32_t h, uint32_t nq, uint32_t np_, uint32_t alpha,
@@ -124,17 +147,23 @@ __global__ __launch_bounds__(kKsThreads) void modup_kernel(uint64_t* __restrict_
     x[i] = gi.neg ? neg_mod(a, q) : a;
   }
   uint64_t* out = ext + (uint64_t)bj * nqp * n + e;
+  if (blockIdx.z == 0) {
 #pragma unroll
-  for (int i = 0; i < K; ++i) {
-    if (i >= (int)alpha) break;
-    out[(uint64_t)(first + i) * n] = x[i];  // the digit's own primes keep their residues
+    for (int i = 0; i < K; ++i) {
+      if (i >= (int)alpha) break;
+      out[(uint64_t)(first + i) * n] = x[i];  // the digit's own primes keep their residues
+    }
   }
   constexpr int S = kMaxDigitPrimes;
-  garner<K, S>(x, v, alpha, kc.moduli + first, kc.digit_garner + (size_t)j * S * S);
+  garner<B60, K, S>(x, v, alpha, kc.moduli + first, kc.digit_garner + (size_t)j * S * S);
   const Tw* ev = kc.digit_eval + (size_t)j * nqp * S;
-  for (uint32_t t = 0; t < nqp; ++t) {
-    if (t >= first && t < first + alpha) continue;
-    out[(uint64_t)t * n] = mixed_radix_eval<K>(v, alpha, ev + (size_t)t * S, kc.moduli[t]);
+  // targets m = 0 .. nqp - alpha - 1 skip the digit's own primes: t = m or m + alpha
+  const uint32_t others = nqp - alpha, per = (others + gridDim.z - 1) / gridDim.z;
+  const uint32_t m0 = blockIdx.z * per, m1 = min(others, m0 + per);
+#pragma unroll 4
+  for (uint32_t m = m0; m < m1; ++m) {
+    const uint32_t t = m < first ? m : m + alpha;
+    out[(uint64_t)t * n] = mixed_radix_eval<B60, K>(v, alpha, ev + (size_t)t * S, kc.moduli[t]);
   }
 }
 
@@ -169,8 +198,10 @@ __global__ __launch_bounds__(kKsThreads) void mac_kernel(uint64_t* __restrict__ 
 }
 
 // ---- ModDown + sigma_g(c0) ---------------------------------------------------------
-// grid.x: coefficient tiles; grid.y: batch * 2 (component).  acc: [batch][2][nq+np][n].
-template <int KP>
+// grid.x: coefficient tiles; grid.y: batch * 2 (component); grid.z: groups of the nq
+// output primes (the Garner digits over P are recomputed per group).
+// acc: [batch][2][nq+np][n].
+template <bool B60, int KP>
 __global__ __launch_bounds__(kKsThreads) void moddown_kernel(uint64_t* __restrict__ out,
                                                              const uint64_t* __restrict__ acc,
                                                              const uint64_t* __restrict__ ct, KsDev kc, uint32_t logn,
@@ -188,15 +219,18 @@ __global__ __launch_bounds__(kKsThreads) void moddown_kernel(uint64_t* __restric
     y[i] = a[(uint64_t)(nq + i) * n];
   }
   constexpr int S = kMaxSpecial;
-  garner<KP, S>(y, v, np_, kc.moduli + nq, kc.p_garner);
+  garner<B60, KP, S>(y, v, np_, kc.moduli + nq, kc.p_garner);
   const uint64_t* c0 = ct + (uint64_t)b * 2 * nq * n;
   const Gather gi = gather_index(e, h, logn);
   uint64_t* o = out + (uint64_t)bc * nq * n + e;
-  for (uint32_t l = 0; l < nq; ++l) {
+  const uint32_t per = (nq + gridDim.z - 1) / gridDim.z;
+  const uint32_t l0 = blockIdx.z * per, l1 = min(nq, l0 + per);
+#pragma unroll 4
+  for (uint32_t l = l0; l < l1; ++l) {
     const uint64_t q = kc.moduli[l];
-    const uint64_t r = mixed_radix_eval<KP>(v, np_, kc.p_eval + (size_t)l * S, q);  // (X mod P) mod q_l
+    const uint64_t r = mixed_radix_eval<B60, KP>(v, np_, kc.p_eval + (size_t)l * S, q);  // (X mod P) mod q_l
     const uint64_t d = sub_mod(a[(uint64_t)l * n], r, q);
-    uint64_t res = csub(shoup(d, kc.p_inv[l], q), q);
+    uint64_t res = csub(shoup<B60>(d, kc.p_inv[l], q), q);
     if (comp == 0) {
       const uint64_t s = c0[(uint64_t)l * n + gi.src];
       res = add_mod(res, gi.neg ? neg_mod(s, q) : s, q);
@@ -213,6 +247,7 @@ using namespace nntt;
 struct ntt_ks_plan {
   const ntt_plan* qp = nullptr;
   uint32_t nq = 0, np = 0, dnum = 0, alpha = 0;
+  bool below60 = false;  // every prime of Q u P below 2^60
   void* d_const = nullptr;
   KsDev dev{};
 };
@@ -311,6 +346,7 @@ extern "C" int keyswitch_plan_create(ntt_ks_plan** out, const ntt_plan* qp, uint
   p->np = np_;
   p->dnum = dnum;
   p->alpha = alpha;
+  p->below60 = range_below60(qp, 0, nqp);
   p->dev.moduli = (const uint64_t*)(base + off[0]);
   p->dev.digit_garner = (const Tw*)(base + off[1]);
   p->dev.digit_eval = (const Tw*)(base + off[2]);
@@ -367,12 +403,25 @@ extern "C" int keyswitch(const ntt_ks_plan* p, uint64_t* out, const uint64_t* ct
   const uint32_t h = (uint32_t)host_invmod(galois_elt % two_n, two_n);
   const uint32_t tiles = (n + kKsThreads - 1) / kKsThreads;
 
-  if (p->alpha <= 8)
-    hipLaunchKernelGGL((modup_kernel<8>), dim3(tiles, (uint32_t)(batch * dnum)), dim3(kKsThreads), 0, s, ext, ct,
-                       p->dev, qp->logn, h, nq, np_, p->alpha, dnum);
-  else
-    hipLaunchKernelGGL((modup_kernel<16>), dim3(tiles, (uint32_t)(batch * dnum)), dim3(kKsThreads), 0, s, ext, ct,
-                       p->dev, qp->logn, h, nq, np_, p->alpha, dnum);
+  // Groups of target primes per coefficient: enough resident waves to hide the
+  // latency of the long dependent Shoup chains (measured on MI355X).
+  const uint32_t up_groups = std::max(1u, std::min(kModUpGroups, nqp - p->alpha));
+  const dim3 up_grid(tiles, (uint32_t)(batch * dnum), up_groups);
+  if (p->below60) {
+    if (p->alpha <= 8)
+      hipLaunchKernelGGL((modup_kernel<true, 8>), up_grid, dim3(kKsThreads), 0, s, ext, ct, p->dev, qp->logn, h, nq,
+                         np_, p->alpha, dnum);
+    else
+      hipLaunchKernelGGL((modup_kernel<true, 16>), up_grid, dim3(kKsThreads), 0, s, ext, ct, p->dev, qp->logn, h,
+                         nq, np_, p->alpha, dnum);
+  } else {
+    if (p->alpha <= 8)
+      hipLaunchKernelGGL((modup_kernel<false, 8>), up_grid, dim3(kKsThreads), 0, s, ext, ct, p->dev, qp->logn, h,
+                         nq, np_, p->alpha, dnum);
+    else
+      hipLaunchKernelGGL((modup_kernel<false, 16>), up_grid, dim3(kKsThreads), 0, s, ext, ct, p->dev, qp->logn, h,
+                         nq, np_, p->alpha, dnum);
+  }
   if (hipGetLastError() != hipSuccess) return NTT_EDEVICE;
   if (launch_ntt(qp, ext, batch * dnum, 0, nqp, false, s) != hipSuccess) return NTT_EDEVICE;
   const uint64_t pairs = (uint64_t)nqp * n / 2;
@@ -380,12 +429,23 @@ extern "C" int keyswitch(const ntt_ks_plan* p, uint64_t* out, const uint64_t* ct
                      dim3(kKsThreads), 0, s, acc, ext, ksk, qp->d_mods, qp->logn, nqp, dnum, pairs);
   if (hipGetLastError() != hipSuccess) return NTT_EDEVICE;
   if (launch_ntt(qp, acc, batch * 2, 0, nqp, true, s) != hipSuccess) return NTT_EDEVICE;
-  if (np_ <= 8)
-    hipLaunchKernelGGL((moddown_kernel<8>), dim3(tiles, (uint32_t)(batch * 2)), dim3(kKsThreads), 0, s, out, acc, ct,
-                       p->dev, qp->logn, h, nq, np_);
-  else
-    hipLaunchKernelGGL((moddown_kernel<16>), dim3(tiles, (uint32_t)(batch * 2)), dim3(kKsThreads), 0, s, out, acc,
-                       ct, p->dev, qp->logn, h, nq, np_);
+  const uint32_t down_groups = std::max(1u, std::min(kModDownGroups, nq));
+  const dim3 down_grid(tiles, (uint32_t)(batch * 2), down_groups);
+  if (p->below60) {
+    if (np_ <= 8)
+      hipLaunchKernelGGL((moddown_kernel<true, 8>), down_grid, dim3(kKsThreads), 0, s, out, acc, ct, p->dev,
+                         qp->logn, h, nq, np_);
+    else
+      hipLaunchKernelGGL((moddown_kernel<true, 16>), down_grid, dim3(kKsThreads), 0, s, out, acc, ct, p->dev,
+                         qp->logn, h, nq, np_);
+  } else {
+    if (np_ <= 8)
+      hipLaunchKernelGGL((moddown_kernel<false, 8>), down_grid, dim3(kKsThreads), 0, s, out, acc, ct, p->dev,
+                         qp->logn, h, nq, np_);
+    else
+      hipLaunchKernelGGL((moddown_kernel<false, 16>), down_grid, dim3(kKsThreads), 0, s, out, acc, ct, p->dev,
+                         qp->logn, h, nq, np_);
+  }
   return hipGetLastError() == hipSuccess ? NTT_OK : NTT_EDEVICE;
 }
 
