@@ -44,6 +44,8 @@ def lib():
             "orc_moddown": (None, [_U64P, _U64P, _U64P, u32, u32, u64]),
             "orc_keyswitch": (i32, [_U64P, _U64P, _U64P, u64, u64, u64, _U64P, u32, u32, u32, i32]),
             "orc_crt_words": (i32, [_U64P, _U64P, u32, _U64P, u32]),
+            "orc_relinearize": (i32, [_U64P, _U64P, _U64P, u64, u64, _U64P, u32, u32, u32, i32]),
+            "orc_rescale": (i32, [_U64P, _U64P, i32, u64, u32, u64, _U64P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -231,3 +233,32 @@ def crt_int(residues, moduli) -> int:
     if got < 0:
         raise ValueError("CRT value does not fit")
     return sum(int(w) << (64 * i) for i, w in enumerate(out))
+
+
+def relinearize(d, rlk, qp, nq: int, dnum: int, threads: int = 0) -> np.ndarray:
+    """d: [batch, 3, nq, n] (or [3, nq, n]); rlk: [dnum, 2, nq+np, n] -> [..., 2, nq, n]."""
+    d, rlk = _u64(d), _u64(rlk)
+    n = d.shape[-1]
+    assert d.shape[-2] == nq and d.shape[-3] == 3
+    batch = d.size // (3 * nq * n)
+    np_ = len(qp) - nq
+    assert rlk.shape == (dnum, 2, nq + np_, n), rlk.shape
+    out = np.zeros(d.shape[:-3] + (2, nq, n), dtype=np.uint64)
+    rc = lib().orc_relinearize(_p(out), _p(d), _p(rlk), batch, n, _p(_u64(qp)), nq, np_, dnum,
+                               threads or default_threads())
+    if rc:
+        raise ValueError("bad relinearisation arguments")
+    return out
+
+
+def rescale(x, primes, mode: int) -> np.ndarray:
+    """x: [..., limbs, n] -> [..., limbs - 1, n]; mode 0 truncating, 1 nearest."""
+    x = _u64(x)
+    n, limbs = x.shape[-1], x.shape[-2]
+    assert limbs == len(primes) and limbs >= 2
+    batch = x.size // (limbs * n)
+    out = np.zeros(x.shape[:-2] + (limbs - 1, n), dtype=np.uint64)
+    rc = lib().orc_rescale(_p(out), _p(x), mode, batch, limbs, n, _p(_u64(primes)))
+    if rc:
+        raise ValueError("bad rescale arguments")
+    return out

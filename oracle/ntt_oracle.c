@@ -618,3 +618,53 @@ int orc_keyswitch(uint64_t *out, const uint64_t *ct, const uint64_t *ksk, uint64
   free(md);
   return rc;
 }
+
+/* ---- relinearisation -------------------------------------------------------- */
+
+int orc_relinearize(uint64_t *out, const uint64_t *d, const uint64_t *rlk, uint64_t batch, uint64_t n,
+                    const uint64_t *qp, uint32_t nq, uint32_t np, uint32_t dnum, int threads) {
+  if (dnum == 0 || nq == 0 || nq % dnum != 0) return -1;
+  uint64_t plane = (uint64_t)nq * n;
+  uint64_t *ct = (uint64_t *)malloc(2 * plane * sizeof(uint64_t));
+  int rc = 0;
+  for (uint64_t bi = 0; bi < batch && rc == 0; ++bi) {
+    const uint64_t *d0 = d + bi * 3 * plane, *d1 = d0 + plane, *d2 = d1 + plane;
+    uint64_t *o = out + bi * 2 * plane;
+    /* switch (d0, d2) with g = 1: gives (d0 + ModDown(acc_0), ModDown(acc_1)) */
+    memcpy(ct, d0, plane * sizeof(uint64_t));
+    memcpy(ct + plane, d2, plane * sizeof(uint64_t));
+    rc = orc_keyswitch(o, ct, rlk, 1, 1, n, qp, nq, np, dnum, threads);
+    for (uint32_t l = 0; l < nq && rc == 0; ++l)
+      for (uint64_t e = 0; e < n; ++e) {
+        uint64_t i = (uint64_t)l * n + e;
+        o[plane + i] = addm(o[plane + i], d1[i], qp[l]);
+      }
+  }
+  free(ct);
+  return rc;
+}
+
+/* ---- rescale ---------------------------------------------------------------- */
+
+int orc_rescale(uint64_t *out, const uint64_t *in, int mode, uint64_t batch, uint32_t limbs, uint64_t n,
+                const uint64_t *primes) {
+  if (limbs < 2 || (mode != 0 && mode != 1)) return -1;
+  crt_basis b;
+  if (crt_basis_init(&b, primes, limbs)) {
+    crt_basis_free(&b);
+    return -1;
+  }
+  uint64_t ql = primes[limbs - 1];
+  big_t half;
+  big_set_u64(&half, mode ? ql / 2 : 0);
+  for (uint64_t bi = 0; bi < batch; ++bi)
+    for (uint64_t e = 0; e < n; ++e) {
+      big_t X, Y;
+      crt_value(&b, in + bi * limbs * n + e, n, &X); /* X in [0, prod q) */
+      big_add(&X, &half);
+      big_div_u64(&Y, &X, ql); /* floor */
+      for (uint32_t l = 0; l + 1 < limbs; ++l) out[(bi * (limbs - 1) + l) * n + e] = big_mod_u64(&Y, primes[l]);
+    }
+  crt_basis_free(&b);
+  return 0;
+}

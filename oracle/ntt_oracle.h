@@ -122,6 +122,26 @@ void orc_moddown(const uint64_t *acc, uint64_t *out, const uint64_t *qp, uint32_
 int orc_keyswitch(uint64_t *out, const uint64_t *ct, const uint64_t *ksk, uint64_t g, uint64_t batch,
                   uint64_t n, const uint64_t *qp, uint32_t nq, uint32_t np, uint32_t dnum, int threads);
 
+/* Relinearisation of a batch of tensor products d = (d0, d1, d2), each
+ * [batch][3][nq][n] in the coefficient domain: the quadratic term is switched with
+ * the relinearisation key rlk [dnum][2][nq+np][n] (NTT domain over Q u P), with no
+ * automorphism (g = 1):  out = (d0 + ModDown(acc_0), d1 + ModDown(acc_1)),
+ * acc_c = INTT(sum_j NTT(ModUp(digit_j(d2))) * rlk[j][c]).  out: [batch][2][nq][n].
+ * The kestrel-llm overview (section 3) lists relin beside mul and rescale in its
+ * CKKS layer.  Returns 0, or -1 on a bad argument. */
+int orc_relinearize(uint64_t *out, const uint64_t *d, const uint64_t *rlk, uint64_t batch, uint64_t n,
+                    const uint64_t *qp, uint32_t nq, uint32_t np, uint32_t dnum, int threads);
+
+/* Rescale by the last prime of a basis (FHElium "Eager, Compile, and native
+ * execution", section "CUDA execution": nearest and truncating rescale kernels).
+ * in: [batch][limbs][n] coefficient domain modulo primes[0..limbs); X = the CRT
+ * value of a column in [0, prod primes).  out: [batch][limbs-1][n] with
+ *   mode 0 (truncating): out[l] = floor(X / q_last) mod q_l,
+ *   mode 1 (nearest):    out[l] = floor((X + floor(q_last / 2)) / q_last) mod q_l.
+ * Returns 0, or -1 on a bad argument. */
+int orc_rescale(uint64_t *out, const uint64_t *in, int mode, uint64_t batch, uint32_t limbs, uint64_t n,
+                const uint64_t *primes);
+
 /* Multi-word CRT helper exposed for tests: value of residues x[0..k) modulo
  * m[0..k) as little-endian 64-bit words into out (capacity `words`).  Returns the
  * number of significant words, or -1 if it does not fit. */

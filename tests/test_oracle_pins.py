@@ -465,3 +465,162 @@ def test_keyswitch_semantic_small_ring(ks_primes, g):
         worst = max(worst, abs(v))
     # bound: dnum * n * |e| * max(Qj)/P + 1 + n (floor terms) ~ 2^15; far below q
     assert worst < (1 << 20), worst
+
+
+# ---- P11: rescale ------------------------------------------------------------------
+
+def _residue_columns(values, primes):
+    return np.array([[v % q for v in values] for q in primes], dtype=np.uint64)
+
+
+@pytest.mark.parametrize("which", ["wide", "narrow", "mixed"])
+def test_rescale_constructed_quotients(ks_primes, primes, which):
+    """X = a q_k + r built from chosen quotient a and remainder r (r at the rounding
+    boundaries and at random): truncation gives a, nearest gives a + [r > h] with
+    h = floor(q_k / 2); for the negative X = Q - (a q_k + r) the centered results
+    are -a - [r > 0] and -a - [r > h]."""
+    Q, _ = ks_primes
+    narrow = primes[workloads.POLYMUL.name]
+    ps = {"wide": list(Q[:6]), "narrow": list(narrow[:4]), "mixed": [narrow[0], Q[1], narrow[1], Q[0]]}[which]
+    qk = ps[-1]
+    h = qk // 2
+    Qm = 1
+    for q in ps:
+        Qm *= q
+    amax = Qm // qk
+    rng = random.Random(1100 + len(which))
+    rs = [0, 1, h - 1, h, h + 1, qk - 1] + [rng.randrange(qk) for _ in range(10)]
+    a_s = [rng.randrange(amax) for _ in rs]
+    a_s[0] = 0
+    a_s[1] = amax - 1
+    pos = [a * qk + r for a, r in zip(a_s, rs)]
+    neg = [Qm - x for x in pos if x]
+    x = np.stack([_residue_columns(pos, ps)])
+    t = orc.rescale(x, ps, 0)[0]
+    nr = orc.rescale(x, ps, 1)[0]
+    for l, q in enumerate(ps[:-1]):
+        assert [int(v) for v in t[l]] == [a % q for a in a_s]
+        assert [int(v) for v in nr[l]] == [(a + (r > h)) % q for a, r in zip(a_s, rs)]
+    keep = [(a, r) for a, r in zip(a_s, rs) if a * qk + r]
+    xn = np.stack([_residue_columns(neg, ps)])
+    t = orc.rescale(xn, ps, 0)[0]
+    nr = orc.rescale(xn, ps, 1)[0]
+    for l, q in enumerate(ps[:-1]):
+        assert [int(v) for v in t[l]] == [(-a - (r > 0)) % q for a, r in keep]
+        assert [int(v) for v in nr[l]] == [(-a - (r > h)) % q for a, r in keep]
+
+
+def test_rescale_twice_is_floor_by_the_product(ks_primes):
+    """floor(floor(X / q1) / q2) = floor(X / (q1 q2)): two truncating rescales agree
+    with one division by the product of the two dropped primes."""
+    Q, _ = ks_primes
+    ps = list(Q[:5])
+    Qm = 1
+    for q in ps:
+        Qm *= q
+    rng = random.Random(1111)
+    xs = [rng.randrange(Qm) for _ in range(64)] + [0, Qm - 1]
+    x = _residue_columns(xs, ps)[None]
+    two = orc.rescale(orc.rescale(x, ps, 0), ps[:-1], 0)[0]
+    d = ps[-1] * ps[-2]
+    for l, q in enumerate(ps[:-2]):
+        assert [int(v) for v in two[l]] == [(v // d) % q for v in xs]
+
+
+def test_rescale_batch_layout(ks_primes):
+    """Batch entries are independent: a [3][L][n] call equals three single calls."""
+    Q, _ = ks_primes
+    ps = list(Q[:4])
+    x = inputs.uniform_residues((3, 4, 32), ps, 1120)
+    both = orc.rescale(x, ps, 1)
+    assert both.shape == (3, 3, 32)
+    for b in range(3):
+        assert np.array_equal(both[b], orc.rescale(x[b], ps, 1))
+
+
+# ---- P12: relinearisation and the full ciphertext product ---------------------------
+
+def test_relinearize_zero_key_and_zero_d2(ks_primes):
+    Q, P = ks_primes
+    qp = list(Q) + list(P)
+    n = 128
+    d = inputs.uniform_residues((1, 3, 24, n), Q, 1200)
+    out = orc.relinearize(d, np.zeros((3, 2, 32, n), dtype=np.uint64), qp, 24, 3)
+    assert np.array_equal(out[0, 0], d[0, 0]) and np.array_equal(out[0, 1], d[0, 1])
+    d2 = d.copy()
+    d2[0, 2] = 0
+    rlk = inputs.uniform_residues((3, 2, 32, n), qp, 1201)
+    out = orc.relinearize(d2, rlk, qp, 24, 3)
+    assert np.array_equal(out[0, 0], d[0, 0]) and np.array_equal(out[0, 1], d[0, 1])
+
+
+def _ciphertext(m_limbs, s, primes, seed):
+    """(b, a) with b = -a s + m + e over the given primes (coefficient domain)."""
+    from tests import keygen
+    n = s.shape[1]
+    a = inputs.uniform_residues((len(primes), n), list(primes), seed)
+    e = keygen.to_limbs(inputs.small_signed(n, 8, seed + 1), primes)
+    b = keygen.padd(keygen.psub(e, keygen.pmul(a, s, primes), primes), m_limbs, primes)
+    return np.stack([b, a])
+
+
+def test_relinearize_semantic_small_ring(ks_primes):
+    """With a real s^2 -> s key at n = 1024, (c0, c1) = relin(d0, d1, d2) satisfies
+    c0 + c1 s = d0 + d1 s + d2 s^2 up to a small error (key noise, floor ModDown)."""
+    from tests import keygen
+    Q, P = ks_primes
+    qp = list(Q) + list(P)
+    n = 1024
+    s = keygen.to_limbs(inputs.small_signed(n, 1, 1210), qp)
+    s2 = keygen.pmul(s, s, qp)
+    rlk = keygen.switching_key(s2, s, qp, 24, 3, 1220)
+    d = inputs.uniform_residues((1, 3, 24, n), Q, 1230)
+    out = orc.relinearize(d, rlk, qp, 24, 3)
+    sQ, s2Q = s[:24], s2[:24]
+    lhs = keygen.padd(out[0, 0], keygen.pmul(out[0, 1], sQ, Q), Q)
+    rhs = keygen.padd(keygen.padd(d[0, 0], keygen.pmul(d[0, 1], sQ, Q), Q), keygen.pmul(d[0, 2], s2Q, Q), Q)
+    worst = keygen.centered_crt_max(keygen.psub(lhs, rhs, Q), Q, stride=5)
+    assert worst < (1 << 20), worst
+
+
+def test_ciphertext_product_decrypts_to_the_scaled_product(ks_primes):
+    """Whole ct x ct multiply through the oracle: NTT, tensor, INTT, relinearise,
+    rescale (nearest).  With m_i = Delta u_i, the result decrypts under s, modulo
+    the remaining primes, to Delta^2 (u_1 * u_2) / q_last up to a small error;
+    the signal is 2^20 per unit of u_1 * u_2."""
+    from tests import keygen
+    Q, P = ks_primes
+    qp = list(Q) + list(P)
+    n = 1024
+    delta = 1 << 40
+    s = keygen.to_limbs(inputs.small_signed(n, 1, 1240), qp)
+    rlk = keygen.switching_key(keygen.pmul(s, s, qp), s, qp, 24, 3, 1250)
+    u1 = [int(v) for v in inputs.small_signed(n, 3, 1260)]
+    u2 = [int(v) for v in inputs.small_signed(n, 3, 1261)]
+    sQ = s[:24]
+    c1 = _ciphertext(keygen.to_limbs([delta * v for v in u1], Q), sQ, Q, 1270)
+    c2 = _ciphertext(keygen.to_limbs([delta * v for v in u2], Q), sQ, Q, 1280)
+    f1 = orc.batch_ntt(c1, Q)
+    f2 = orc.batch_ntt(c2, Q)
+    d = orc.batch_ntt(orc.batch_tensor(f1, f2, Q), Q, inverse=True)
+    ct = orc.relinearize(d[None], rlk, qp, 24, 3)[0]
+    r = orc.rescale(ct, Q, 1)
+    Qr = Q[:-1]
+    dec = keygen.padd(r[0], keygen.pmul(r[1], sQ[:-1], Qr), Qr)
+    got = keygen.centered_values(dec, Qr)
+    # integer negacyclic product u1 * u2
+    uu = [0] * n
+    for i, a in enumerate(u1):
+        if a:
+            for j, b in enumerate(u2):
+                k = i + j
+                if k < n:
+                    uu[k] += a * b
+                else:
+                    uu[k - n] -= a * b
+    scale = delta * delta
+    worst = max(abs(g * Q[-1] - scale * v) for g, v in zip(got, uu)) / Q[-1]
+    # rounding of (c0, c1) contributes at most (1 + ||s||_1) / 2 <= n / 2 + 1; key
+    # and encryption noise are far below one unit after the division by q_last
+    assert worst < n / 2 + 2, worst
+    assert any(uu)
