@@ -150,6 +150,21 @@ int ct_tensor_ntt(const ntt_plan *plan, uint64_t *out, const uint64_t *a, const 
 int automorph(const ntt_plan *plan, uint64_t *out, const uint64_t *in, uint64_t galois_elt, int domain,
               uint64_t batch, uint32_t limb_begin, uint32_t num_limbs, void *stream);
 
+/* Rescale by the last prime of a limb range (FHElium "Eager, Compile, and native
+ * execution", section "CUDA execution": nearest and truncating rescale kernels;
+ * "rescale" of the kestrel-llm overview's CKKS layer, section 3).
+ *   in  : [batch][num_limbs][n], coefficient domain, canonical residues modulo the
+ *         plan primes [limb_begin, limb_begin + num_limbs); num_limbs >= 2;
+ *   out : [batch][num_limbs - 1][n] modulo the same primes without the last one,
+ *         q_k = prime (limb_begin + num_limbs - 1).  With X in [0, prod q) the CRT
+ *         value of a coefficient's residues:
+ *           mode 0 (truncating): out = floor(X / q_k)              mod q_l,
+ *           mode 1 (nearest):    out = floor((X + floor(q_k / 2)) / q_k) mod q_l.
+ * Exact integer arithmetic, so bit-exact.  out must not overlap in (NTT_EOVERLAP);
+ * mode other than 0 / 1 or num_limbs < 2 is NTT_EINVAL. */
+int rescale(const ntt_plan *plan, uint64_t *out, const uint64_t *in, int mode, uint64_t batch, uint32_t limb_begin,
+            uint32_t num_limbs, void *stream);
+
 /* Key-switch plan over a Q u P basis: the first num_q primes of qp_plan form Q
  * and the next num_p form P (num_q + num_p <= primes in qp_plan); Q is split into
  * dnum digits of num_q / dnum consecutive primes (num_q % dnum == 0,
@@ -180,6 +195,20 @@ int keyswitch_workspace_size(const ntt_ks_plan *plan, uint64_t batch, size_t *by
  * not overlapping out/ct/ksk.  out must not overlap ct, ksk or workspace. */
 int keyswitch(const ntt_ks_plan *plan, uint64_t *out, const uint64_t *ct, const uint64_t *ksk,
               uint64_t galois_elt, uint64_t batch, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Relinearisation of tensor products (the "relin" operation of the kestrel-llm
+ * overview's CKKS layer, section 3; it closes the ciphertext-ciphertext multiply
+ * whose tensor step is ct_tensor_ntt):
+ *   d   : [batch][3][num_q][n], coefficient domain (d0, d1, d2);
+ *   rlk : [dnum][2][num_q + num_p][n], NTT domain over Q u P, the key that carries
+ *         s^2 to s (same layout as a rotation key);
+ *   out : [batch][2][num_q][n] = ( d0 + ModDown(acc_0), d1 + ModDown(acc_1) ) with
+ *         acc_c = INTT( sum_j NTT(ModUp(digit_j(d2))) * rlk[j][c] ).
+ * The same ModUp / key product / ModDown as keyswitch with no automorphism.
+ * workspace: as for keyswitch (keyswitch_workspace_size bytes for `batch`).  out
+ * must not overlap d, rlk or workspace (NTT_EOVERLAP). */
+int relinearize(const ntt_ks_plan *plan, uint64_t *out, const uint64_t *d, const uint64_t *rlk, uint64_t batch,
+                void *workspace, size_t workspace_bytes, void *stream);
 
 void keyswitch_plan_destroy(ntt_ks_plan *plan);
 

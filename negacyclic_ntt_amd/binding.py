@@ -54,6 +54,8 @@ def lib():
             "keyswitch_workspace_size": (i32, [_VP, u64, ctypes.POINTER(sz)]),
             "keyswitch": (i32, [_VP, _VP, _VP, _VP, u64, u64, _VP, sz, _VP]),
             "keyswitch_plan_destroy": (None, [_VP]),
+            "relinearize": (i32, [_VP, _VP, _VP, _VP, u64, _VP, sz, _VP]),
+            "rescale": (i32, [_VP, _VP, _VP, i32, u64, u32, u32, _VP]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -216,6 +218,18 @@ def automorph(plan: Plan, out, x, galois_elt: int, domain: int = 0, limb_begin: 
     return out
 
 
+def rescale(plan: Plan, out, x, mode: int = 0, limb_begin: int = 0, stream=None):
+    """out [..., limbs - 1, n] = x [..., limbs, n] divided by its last prime;
+    mode 0 truncating (floor), 1 nearest (floor of X / q + 1/2)."""
+    batch, limbs = _check_tensor(x, plan, "x")
+    _check_tensor(out, plan, "out")
+    if tuple(out.shape) != tuple(x.shape[:-2]) + (limbs - 1, plan.n):
+        raise ValueError("out must be [..., limbs - 1, n]")
+    _check(lib().rescale(plan.handle, _VP(out.data_ptr()), _VP(x.data_ptr()), mode, batch, limb_begin, limbs,
+                         _stream_ptr(x, stream)), "rescale")
+    return out
+
+
 class KeySwitchPlan:
     """Hybrid key-switch constants over a Q u P plan (see keyswitch_plan_create)."""
 
@@ -272,6 +286,26 @@ def keyswitch(ks: KeySwitchPlan, out, ct, ksk, galois_elt: int, ws=None, stream=
     _check(lib().keyswitch(ks.handle, _VP(out.data_ptr()), _VP(ct.data_ptr()), _VP(ksk.data_ptr()), galois_elt,
                            batch, _VP(ws.data_ptr()), ws.numel() * ws.element_size(), _stream_ptr(ct, stream)),
            "keyswitch")
+    return out
+
+
+def relinearize(ks: KeySwitchPlan, out, d, rlk, ws=None, stream=None):
+    """Relinearisation; d [batch, 3, num_q, n] -> out [batch, 2, num_q, n]; rlk [dnum, 2, num_q + num_p, n]."""
+    plan = ks.qp_plan
+    batch, limbs = _check_tensor(d, plan, "d", lead=1)
+    _check_tensor(out, plan, "out", lead=1)
+    _check_tensor(rlk, plan, "rlk", lead=1)
+    if limbs != ks.num_q or d.shape[-3] != 3:
+        raise ValueError("d must be [batch, 3, num_q, n]")
+    if tuple(out.shape) != tuple(d.shape[:-3]) + (2, ks.num_q, plan.n):
+        raise ValueError("out must be [batch, 2, num_q, n]")
+    if tuple(rlk.shape) != (ks.dnum, 2, ks.num_q + ks.num_p, plan.n):
+        raise ValueError("rlk must be [dnum, 2, num_q + num_p, n]")
+    if ws is None:
+        ws = workspace(ks, batch)
+    _check(lib().relinearize(ks.handle, _VP(out.data_ptr()), _VP(d.data_ptr()), _VP(rlk.data_ptr()), batch,
+                             _VP(ws.data_ptr()), ws.numel() * ws.element_size(), _stream_ptr(d, stream)),
+           "relinearize")
     return out
 
 

@@ -121,3 +121,18 @@ extern "C" int automorph(const ntt_plan* p, uint64_t* out, const uint64_t* in, u
   return status_of(launch_automorph(p, out, in, galois_elt, domain, batch, limb_begin, num_limbs,
                                     (hipStream_t)stream));
 }
+
+extern "C" int rescale(const ntt_plan* p, uint64_t* out, const uint64_t* in, int mode, uint64_t batch,
+                       uint32_t limb_begin, uint32_t num_limbs, void* stream) {
+  uint64_t elems = 0;
+  int rc = check_plan_range(p, batch, limb_begin, num_limbs, 1, &elems);
+  if (rc) return rc;
+  if (num_limbs < 2 || (mode != 0 && mode != 1)) return NTT_EINVAL;
+  if (!elems) return NTT_OK;
+  if (!out || !in || !aligned16(out) || !aligned16(in)) return NTT_EINVAL;
+  const uint64_t out_elems = elems / num_limbs * (num_limbs - 1);
+  if (overlaps(out, out_elems * 8, in, elems * 8)) return NTT_EOVERLAP;
+  DeviceGuard g(p->device);
+  if (!g.ok) return NTT_EDEVICE;
+  return status_of(launch_rescale(p, out, in, batch, limb_begin, num_limbs, mode == 1, (hipStream_t)stream));
+}

@@ -6,6 +6,8 @@
 // maps kernel grids onto the tensor axes limb x coefficient tile x batch; here the
 // [batch][limb][n] tensor is treated as one flat array whose row r has limb
 // r % num_limbs, which covers the same axes with a 1-D grid.
+#include <algorithm>
+
 #include "internal.h"
 
 namespace nntt {
@@ -126,6 +128,52 @@ __global__ __launch_bounds__(kThreads) void automorph_ntt_kernel(uint64_t* __res
   out[idx] = in[(row << logn) + p];
 }
 
+// Rescale by the last prime q_k of the input range (FHElium "Eager, Compile, and native
+// execution", section "CUDA execution": nearest and truncating rescale).  With X the
+// CRT value of a column and x_k = X mod q_k,
+//   floor(X / q_k) = (X - x_k) / q_k  ==  (x_l - x_k) * q_k^-1   (mod q_l);
+// nearest adds h = floor(q_k / 2) to X first: x_k <- (x_k + h) mod q_k, x_l <- x_l + h.
+// x_k is not reduced modulo q_l: y = x_l + (h mod q_l) + M - x_k with M a multiple of
+// q_l that is >= q_k stays non-negative and below 2^64, and one Shoup product by
+// q_k^-1 (valid for any 64-bit y) gives the quotient residue.
+// grid.x: tiles of coefficient pairs; grid.y: batch; grid.z: groups of output limbs.
+__global__ __launch_bounds__(kThreads) void rescale_kernel(uint64_t* __restrict__ out,
+                                                           const uint64_t* __restrict__ in,
+                                                           const ModInfo* __restrict__ mods,
+                                                           const RescaleC* __restrict__ tri, uint32_t logn,
+                                                           uint32_t limb_begin, uint32_t num_limbs,
+                                                           uint32_t nearest) {
+  const uint32_t p = blockIdx.x * kThreads + threadIdx.x;
+  const uint32_t n = 1u << logn;
+  if (2 * p >= n) return;
+  const uint32_t outl = num_limbs - 1, k = limb_begin + outl;
+  const uint64_t* x = in + (uint64_t)blockIdx.y * num_limbs * n + 2 * p;
+  uint64_t* o = out + (uint64_t)blockIdx.y * outl * n + 2 * p;
+  const uint64_t qk = mods[k].q;
+  const u64x2 xv = ld_stream(x + (uint64_t)outl * n);
+  uint64_t xk0 = xv.x, xk1 = xv.y;
+  if (nearest) {
+    const uint64_t h = qk >> 1;
+    xk0 = csub(xk0 + h, qk);
+    xk1 = csub(xk1 + h, qk);
+  }
+  const RescaleC* row = tri + rescale_index(k, limb_begin);
+  const uint32_t per = (outl + gridDim.z - 1) / gridDim.z;
+  const uint32_t l0 = blockIdx.z * per, l1 = min(outl, l0 + per);
+#pragma unroll 4
+  for (uint32_t l = l0; l < l1; ++l) {
+    const RescaleC c = row[l];
+    const uint64_t q = mods[limb_begin + l].q;
+    const uint64_t add = c.m + (nearest ? c.half : 0);
+    const u64x2 xl = ld_stream(x + (uint64_t)l * n);
+    const Wide::Tw w{c.inv, c.inv_shoup};
+    u64x2 r;
+    r.x = csub(Wide::mul(xl.x + add - xk0, w, q), q);
+    r.y = csub(Wide::mul(xl.y + add - xk1, w, q), q);
+    st_stream(o + (uint64_t)l * n, r);
+  }
+}
+
 uint32_t blocks_for(uint64_t work) { return (uint32_t)((work + kThreads - 1) / kThreads); }
 
 }  // namespace
@@ -162,6 +210,26 @@ hipError_t launch_automorph(const ntt_plan* p, uint64_t* out, const uint64_t* in
                        (uint32_t)(g % two_n), total);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_rescale(const ntt_plan* p, uint64_t* out, const uint64_t* in, uint64_t batch, uint32_t limb_begin,
+                          uint32_t num_limbs, bool nearest, hipStream_t s) {
+  if (!batch) return hipSuccess;
+  const uint32_t tiles = (p->n / 2 + kThreads - 1) / kThreads;
+  // Enough blocks to fill the chip: split the output limbs into groups when the
+  // batch is small (each group re-reads the dropped limb, one row of n words).
+  const uint64_t base = (uint64_t)tiles * batch;
+  const uint32_t want = (uint32_t)std::min<uint64_t>(num_limbs - 1, (2048 + base - 1) / base);
+  const uint32_t groups = std::max(1u, want);
+  for (uint64_t b0 = 0; b0 < batch; b0 += 65535) {
+    const uint64_t nb = std::min<uint64_t>(65535, batch - b0);
+    hipLaunchKernelGGL(rescale_kernel, dim3(tiles, (uint32_t)nb, groups), dim3(kThreads), 0, s,
+                       out + b0 * (num_limbs - 1) * p->n, in + b0 * num_limbs * p->n, p->d_mods, p->d_rescale,
+                       p->logn, limb_begin, num_limbs, nearest ? 1u : 0u);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace nntt

@@ -20,6 +20,15 @@ struct ModInfo {
   Barrett br;
 };
 
+// Constants to divide by prime k and express the quotient modulo prime l < k (rescale).
+// Stored as a triangle: entry k (k - 1) / 2 + l.
+struct RescaleC {
+  uint64_t inv, inv_shoup;  // q_k^-1 mod q_l and floor(inv * 2^64 / q_l)
+  uint64_t m;               // q_l * ceil(q_k / q_l): a multiple of q_l that is >= q_k
+  uint64_t half;            // floor(q_k / 2) mod q_l
+};
+__host__ __device__ inline size_t rescale_index(uint32_t k, uint32_t l) { return (size_t)k * (k - 1) / 2 + l; }
+
 constexpr uint32_t kMaxLogN = 16;
 constexpr uint32_t kMaxPrimes = 4096;
 
@@ -41,6 +50,7 @@ struct ntt_plan {
   nntt::Narrow::Tw* d_fwd32 = nullptr;  // [L][n], entries of wide primes are zero
   nntt::Narrow::Tw* d_inv32 = nullptr;
   nntt::ModInfo* d_mods = nullptr;    // [L]
+  nntt::RescaleC* d_rescale = nullptr;  // triangle over the plan's primes, L (L - 1) / 2 entries
 };
 
 namespace nntt {
@@ -77,5 +87,8 @@ hipError_t launch_tensor(const ntt_plan* p, uint64_t* out, const uint64_t* a, co
                          uint32_t limb_begin, uint32_t num_limbs, hipStream_t s);
 hipError_t launch_automorph(const ntt_plan* p, uint64_t* out, const uint64_t* in, uint64_t g, int domain,
                             uint64_t batch, uint32_t limb_begin, uint32_t num_limbs, hipStream_t s);
+// in: [batch][num_limbs][n] over primes [limb_begin, limb_begin + num_limbs); out: [batch][num_limbs - 1][n].
+hipError_t launch_rescale(const ntt_plan* p, uint64_t* out, const uint64_t* in, uint64_t batch, uint32_t limb_begin,
+                          uint32_t num_limbs, bool nearest, hipStream_t s);
 
 }  // namespace nntt

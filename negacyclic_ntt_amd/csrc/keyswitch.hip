@@ -125,17 +125,19 @@ struct KsDev {
 // group's share of the nq + np - alpha other primes: the groups multiply the
 // number of resident waves (the Garner digits are recomputed per group).
 // ext: [batch][dnum][nq+np][n].
+// src: the polynomial that is decomposed, [batch][nq][n] with batch stride src_stride
+// (c1 of a ciphertext, or d2 of a tensor product).
 template <bool B60, int K>
 __global__ __launch_bounds__(kKsThreads) void modup_kernel(uint64_t* __restrict__ ext,
-                                                           const uint64_t* __restrict__ ct, KsDev kc, uint32_t logn,
-                                                           uint32_t h, uint32_t nq, uint32_t np_, uint32_t alpha,
-                                                           uint32_t dnum) {
+                                                           const uint64_t* __restrict__ src, uint64_t src_stride,
+                                                           KsDev kc, uint32_t logn, uint32_t h, uint32_t nq,
+                                                           uint32_t np_, uint32_t alpha, uint32_t dnum) {
   const uint32_t n = 1u << logn;
   const uint32_t e = blockIdx.x * kKsThreads + threadIdx.x;
   if (e >= n) return;
   const uint32_t bj = blockIdx.y, b = bj / dnum, j = bj % dnum;
   const uint32_t nqp = nq + np_;
-  const uint64_t* c1 = ct + ((uint64_t)b * 2 + 1) * nq * n;
+  const uint64_t* c1 = src + (uint64_t)b * src_stride;
   const Gather gi = gather_index(e, h, logn);
   const uint32_t first = j * alpha;
   uint64_t x[K], v[K];
@@ -197,15 +199,18 @@ __global__ __launch_bounds__(kKsThreads) void mac_kernel(uint64_t* __restrict__ 
   *reinterpret_cast<ulonglong2*>(o + plane) = s1;
 }
 
-// ---- ModDown + sigma_g(c0) ---------------------------------------------------------
+// ---- ModDown + the additive part -----------------------------------------------------
 // grid.x: coefficient tiles; grid.y: batch * 2 (component); grid.z: groups of the nq
 // output primes (the Garner digits over P are recomputed per group).
-// acc: [batch][2][nq+np][n].
+// acc: [batch][2][nq+np][n].  Output component c gets sigma_g(add[b][c]) added when
+// bit c of add_mask is set (add: [batch][*][nq][n], batch stride add_stride): c0 for
+// a rotation, (d0, d1) for a relinearisation.
 template <bool B60, int KP>
 __global__ __launch_bounds__(kKsThreads) void moddown_kernel(uint64_t* __restrict__ out,
                                                              const uint64_t* __restrict__ acc,
-                                                             const uint64_t* __restrict__ ct, KsDev kc, uint32_t logn,
-                                                             uint32_t h, uint32_t nq, uint32_t np_) {
+                                                             const uint64_t* __restrict__ add, uint64_t add_stride,
+                                                             uint32_t add_mask, KsDev kc, uint32_t logn, uint32_t h,
+                                                             uint32_t nq, uint32_t np_) {
   const uint32_t n = 1u << logn;
   const uint32_t e = blockIdx.x * kKsThreads + threadIdx.x;
   if (e >= n) return;
@@ -220,7 +225,8 @@ __global__ __launch_bounds__(kKsThreads) void moddown_kernel(uint64_t* __restric
   }
   constexpr int S = kMaxSpecial;
   garner<B60, KP, S>(y, v, np_, kc.moduli + nq, kc.p_garner);
-  const uint64_t* c0 = ct + (uint64_t)b * 2 * nq * n;
+  const bool adds = (add_mask >> comp) & 1u;
+  const uint64_t* c0 = add + (uint64_t)b * add_stride + (uint64_t)comp * nq * n;
   const Gather gi = gather_index(e, h, logn);
   uint64_t* o = out + (uint64_t)bc * nq * n + e;
   const uint32_t per = (nq + gridDim.z - 1) / gridDim.z;
@@ -231,7 +237,7 @@ __global__ __launch_bounds__(kKsThreads) void moddown_kernel(uint64_t* __restric
     const uint64_t r = mixed_radix_eval<B60, KP>(v, np_, kc.p_eval + (size_t)l * S, q);  // (X mod P) mod q_l
     const uint64_t d = sub_mod(a[(uint64_t)l * n], r, q);
     uint64_t res = csub(shoup<B60>(d, kc.p_inv[l], q), q);
-    if (comp == 0) {
+    if (adds) {
       const uint64_t s = c0[(uint64_t)l * n + gi.src];
       res = add_mod(res, gi.neg ? neg_mod(s, q) : s, q);
     }
@@ -373,80 +379,141 @@ bool ranges_overlap(const void* a, uint64_t na, const void* b, uint64_t nb) {
   const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
   return na && nb && x < y + nb && y < x + na;
 }
-}  // namespace
 
-extern "C" int keyswitch(const ntt_ks_plan* p, uint64_t* out, const uint64_t* ct, const uint64_t* ksk,
-                         uint64_t galois_elt, uint64_t batch, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!p) return NTT_EINVAL;
+// What one key-switch pipeline reads besides the key: the decomposed polynomial and
+// the polynomials added to the ModDown output (both gathered through sigma_g).
+struct KsIo {
+  const uint64_t* src;  // first batch's decomposed polynomial
+  uint64_t src_stride;  // elements between batches
+  const uint64_t* add;  // first batch's component 0 of the additive input
+  uint64_t add_stride;
+  uint32_t add_mask;  // bit c: add component c to output c
+  uint64_t in_bytes;  // whole input extent, for the overlap checks
+  const uint64_t* in;
+};
+
+// Validation shared by the entry points; returns NTT_OK or the error.
+int ks_check(const ntt_ks_plan* p, uint64_t* out, const KsIo& io, const uint64_t* ksk, uint64_t batch,
+             void* workspace, size_t workspace_bytes) {
   const ntt_plan* qp = p->qp;
-  const uint32_t n = qp->n, nq = p->nq, np_ = p->np, nqp = nq + np_, dnum = p->dnum;
-  if (!(galois_elt & 1) || galois_elt >= 2ull * n) return NTT_EINVAL;
-  if (batch == 0) return NTT_OK;
+  const uint32_t n = qp->n, nq = p->nq, nqp = nq + p->np;
   if (batch > 4096) return NTT_EUNSUPPORTED;
-  if (!out || !ct || !ksk || !workspace) return NTT_EINVAL;
-  if (((uintptr_t)out | (uintptr_t)ct | (uintptr_t)ksk) & 15u) return NTT_EINVAL;
+  if (!out || !io.in || !ksk || !workspace) return NTT_EINVAL;
+  if (((uintptr_t)out | (uintptr_t)io.in | (uintptr_t)ksk) & 15u) return NTT_EINVAL;
   if ((uintptr_t)workspace & 255u) return NTT_EINVAL;
   const uint64_t need = ws_elems(p, batch) * 8;
   if (workspace_bytes < need) return NTT_EINVAL;
-  const uint64_t ct_bytes = batch * 2ull * nq * n * 8, ksk_bytes = (uint64_t)dnum * 2 * nqp * n * 8;
-  if (ranges_overlap(out, ct_bytes, ct, ct_bytes) || ranges_overlap(out, ct_bytes, ksk, ksk_bytes) ||
-      ranges_overlap(out, ct_bytes, workspace, need) || ranges_overlap(workspace, need, ct, ct_bytes) ||
+  const uint64_t out_bytes = batch * 2ull * nq * n * 8, ksk_bytes = (uint64_t)p->dnum * 2 * nqp * n * 8;
+  if (ranges_overlap(out, out_bytes, io.in, io.in_bytes) || ranges_overlap(out, out_bytes, ksk, ksk_bytes) ||
+      ranges_overlap(out, out_bytes, workspace, need) || ranges_overlap(workspace, need, io.in, io.in_bytes) ||
       ranges_overlap(workspace, need, ksk, ksk_bytes))
     return NTT_EOVERLAP;
+  return NTT_OK;
+}
 
+template <bool B60, int K>
+void launch_modup(dim3 grid, hipStream_t s, uint64_t* ext, const KsIo& io, const ntt_ks_plan* p, uint32_t h) {
+  hipLaunchKernelGGL((modup_kernel<B60, K>), grid, dim3(kKsThreads), 0, s, ext, io.src, io.src_stride, p->dev,
+                     p->qp->logn, h, p->nq, p->np, p->alpha, p->dnum);
+}
+
+template <bool B60, int KP>
+void launch_moddown(dim3 grid, hipStream_t s, uint64_t* out, const uint64_t* acc, const KsIo& io,
+                    const ntt_ks_plan* p, uint32_t h) {
+  hipLaunchKernelGGL((moddown_kernel<B60, KP>), grid, dim3(kKsThreads), 0, s, out, acc, io.add, io.add_stride,
+                     io.add_mask, p->dev, p->qp->logn, h, p->nq, p->np);
+}
+
+// The five launches of one key-switch (arguments validated).  grid.y carries batch x
+// digits (ModUp) and batch x 2 (ModDown); a batch whose product would exceed the
+// grid's y range is split into chunks.
+int ks_run(const ntt_ks_plan* p, uint64_t* out, const KsIo& io, const uint64_t* ksk, uint64_t galois_elt,
+           uint64_t batch, void* workspace, hipStream_t s) {
+  const ntt_plan* qp = p->qp;
+  const uint32_t n = qp->n, nq = p->nq, nqp = nq + p->np, dnum = p->dnum;
   DeviceGuard g(qp->device);
   if (!g.ok) return NTT_EDEVICE;
-  hipStream_t s = (hipStream_t)stream;
   uint64_t* ext = (uint64_t*)workspace;
   uint64_t* acc = ext + batch * (uint64_t)dnum * nqp * n;
   const uint32_t two_n = 2 * n;
   const uint32_t h = (uint32_t)host_invmod(galois_elt % two_n, two_n);
   const uint32_t tiles = (n + kKsThreads - 1) / kKsThreads;
+  constexpr uint64_t kMaxGridY = 65535;
 
   // Groups of target primes per coefficient: enough resident waves to hide the
   // latency of the long dependent Shoup chains (measured on MI355X).
   const uint32_t up_groups = std::max(1u, std::min(kModUpGroups, nqp - p->alpha));
-  const dim3 up_grid(tiles, (uint32_t)(batch * dnum), up_groups);
-  if (p->below60) {
-    if (p->alpha <= 8)
-      hipLaunchKernelGGL((modup_kernel<true, 8>), up_grid, dim3(kKsThreads), 0, s, ext, ct, p->dev, qp->logn, h, nq,
-                         np_, p->alpha, dnum);
-    else
-      hipLaunchKernelGGL((modup_kernel<true, 16>), up_grid, dim3(kKsThreads), 0, s, ext, ct, p->dev, qp->logn, h,
-                         nq, np_, p->alpha, dnum);
-  } else {
-    if (p->alpha <= 8)
-      hipLaunchKernelGGL((modup_kernel<false, 8>), up_grid, dim3(kKsThreads), 0, s, ext, ct, p->dev, qp->logn, h,
-                         nq, np_, p->alpha, dnum);
-    else
-      hipLaunchKernelGGL((modup_kernel<false, 16>), up_grid, dim3(kKsThreads), 0, s, ext, ct, p->dev, qp->logn, h,
-                         nq, np_, p->alpha, dnum);
+  const uint64_t up_chunk = std::max<uint64_t>(1, kMaxGridY / dnum);
+  for (uint64_t b0 = 0; b0 < batch; b0 += up_chunk) {
+    const uint64_t nb = std::min(up_chunk, batch - b0);
+    KsIo c = io;
+    c.src += b0 * io.src_stride;
+    const dim3 grid(tiles, (uint32_t)(nb * dnum), up_groups);
+    uint64_t* e = ext + b0 * dnum * nqp * n;
+    if (p->below60) {
+      if (p->alpha <= 8) launch_modup<true, 8>(grid, s, e, c, p, h);
+      else launch_modup<true, 16>(grid, s, e, c, p, h);
+    } else {
+      if (p->alpha <= 8) launch_modup<false, 8>(grid, s, e, c, p, h);
+      else launch_modup<false, 16>(grid, s, e, c, p, h);
+    }
+    if (hipGetLastError() != hipSuccess) return NTT_EDEVICE;
   }
-  if (hipGetLastError() != hipSuccess) return NTT_EDEVICE;
   if (launch_ntt(qp, ext, batch * dnum, 0, nqp, false, s) != hipSuccess) return NTT_EDEVICE;
   const uint64_t pairs = (uint64_t)nqp * n / 2;
-  hipLaunchKernelGGL(mac_kernel, dim3((uint32_t)((pairs + kKsThreads - 1) / kKsThreads), (uint32_t)batch),
-                     dim3(kKsThreads), 0, s, acc, ext, ksk, qp->d_mods, qp->logn, nqp, dnum, pairs);
-  if (hipGetLastError() != hipSuccess) return NTT_EDEVICE;
+  for (uint64_t b0 = 0; b0 < batch; b0 += kMaxGridY) {
+    const uint64_t nb = std::min(kMaxGridY, batch - b0);
+    hipLaunchKernelGGL(mac_kernel, dim3((uint32_t)((pairs + kKsThreads - 1) / kKsThreads), (uint32_t)nb),
+                       dim3(kKsThreads), 0, s, acc + b0 * 2 * nqp * n, ext + b0 * dnum * nqp * n, ksk, qp->d_mods,
+                       qp->logn, nqp, dnum, pairs);
+    if (hipGetLastError() != hipSuccess) return NTT_EDEVICE;
+  }
   if (launch_ntt(qp, acc, batch * 2, 0, nqp, true, s) != hipSuccess) return NTT_EDEVICE;
   const uint32_t down_groups = std::max(1u, std::min(kModDownGroups, nq));
-  const dim3 down_grid(tiles, (uint32_t)(batch * 2), down_groups);
-  if (p->below60) {
-    if (np_ <= 8)
-      hipLaunchKernelGGL((moddown_kernel<true, 8>), down_grid, dim3(kKsThreads), 0, s, out, acc, ct, p->dev,
-                         qp->logn, h, nq, np_);
-    else
-      hipLaunchKernelGGL((moddown_kernel<true, 16>), down_grid, dim3(kKsThreads), 0, s, out, acc, ct, p->dev,
-                         qp->logn, h, nq, np_);
-  } else {
-    if (np_ <= 8)
-      hipLaunchKernelGGL((moddown_kernel<false, 8>), down_grid, dim3(kKsThreads), 0, s, out, acc, ct, p->dev,
-                         qp->logn, h, nq, np_);
-    else
-      hipLaunchKernelGGL((moddown_kernel<false, 16>), down_grid, dim3(kKsThreads), 0, s, out, acc, ct, p->dev,
-                         qp->logn, h, nq, np_);
+  const uint64_t down_chunk = kMaxGridY / 2;
+  for (uint64_t b0 = 0; b0 < batch; b0 += down_chunk) {
+    const uint64_t nb = std::min(down_chunk, batch - b0);
+    KsIo c = io;
+    c.add += b0 * io.add_stride;
+    const dim3 grid(tiles, (uint32_t)(nb * 2), down_groups);
+    uint64_t* o = out + b0 * 2 * nq * n;
+    const uint64_t* a = acc + b0 * 2 * nqp * n;
+    if (p->below60) {
+      if (p->np <= 8) launch_moddown<true, 8>(grid, s, o, a, c, p, h);
+      else launch_moddown<true, 16>(grid, s, o, a, c, p, h);
+    } else {
+      if (p->np <= 8) launch_moddown<false, 8>(grid, s, o, a, c, p, h);
+      else launch_moddown<false, 16>(grid, s, o, a, c, p, h);
+    }
+    if (hipGetLastError() != hipSuccess) return NTT_EDEVICE;
   }
-  return hipGetLastError() == hipSuccess ? NTT_OK : NTT_EDEVICE;
+  return NTT_OK;
+}
+}  // namespace
+
+extern "C" int keyswitch(const ntt_ks_plan* p, uint64_t* out, const uint64_t* ct, const uint64_t* ksk,
+                         uint64_t galois_elt, uint64_t batch, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!p) return NTT_EINVAL;
+  const uint32_t n = p->qp->n;
+  const uint64_t plane = (uint64_t)p->nq * n;
+  if (!(galois_elt & 1) || galois_elt >= 2ull * n) return NTT_EINVAL;
+  if (batch == 0) return NTT_OK;
+  const KsIo io{ct ? ct + plane : nullptr, 2 * plane, ct, 2 * plane, 1u, batch * 2 * plane * 8, ct};
+  const int rc = ks_check(p, out, io, ksk, batch, workspace, workspace_bytes);
+  if (rc) return rc;
+  return ks_run(p, out, io, ksk, galois_elt, batch, workspace, (hipStream_t)stream);
+}
+
+extern "C" int relinearize(const ntt_ks_plan* p, uint64_t* out, const uint64_t* d, const uint64_t* rlk,
+                           uint64_t batch, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!p) return NTT_EINVAL;
+  const uint64_t plane = (uint64_t)p->nq * p->qp->n;
+  if (batch == 0) return NTT_OK;
+  // decompose d2, add (d0, d1); no automorphism (g = 1)
+  const KsIo io{d ? d + 2 * plane : nullptr, 3 * plane, d, 3 * plane, 3u, batch * 3 * plane * 8, d};
+  const int rc = ks_check(p, out, io, rlk, batch, workspace, workspace_bytes);
+  if (rc) return rc;
+  return ks_run(p, out, io, rlk, 1, batch, workspace, (hipStream_t)stream);
 }
 
 extern "C" void keyswitch_plan_destroy(ntt_ks_plan* p) {

@@ -151,10 +151,40 @@ static void free_device(ntt_plan* p) {
   (void)hipFree(p->d_fwd32);
   (void)hipFree(p->d_inv32);
   (void)hipFree(p->d_mods);
+  (void)hipFree(p->d_rescale);
   p->d_fwd = p->d_inv = nullptr;
   p->d_fwd60 = p->d_inv60 = nullptr;
   p->d_fwd32 = p->d_inv32 = nullptr;
   p->d_mods = nullptr;
+  p->d_rescale = nullptr;
+}
+
+// Rescale constants for every pair l < k.  The inverses of q_k mod q_l for all k > l
+// share one modular inversion per l (Montgomery's simultaneous inversion: invert the
+// running product once, then peel the factors off from the back).
+static int rescale_triangle(const uint64_t* primes, uint32_t L, std::vector<RescaleC>* out) {
+  try {
+    out->assign(rescale_index(L, 0), RescaleC{0, 0, 0, 0});
+  } catch (const std::bad_alloc&) {
+    return NTT_ENOMEM;
+  }
+  std::vector<uint64_t> pre(L + 1);
+  for (uint32_t l = 0; l + 1 < L; ++l) {
+    const uint64_t ql = primes[l];
+    pre[l + 1] = 1;  // pre[k + 1] = prod_{l < j <= k} (q_j mod q_l)
+    for (uint32_t k = l + 1; k < L; ++k) pre[k + 1] = host_mulmod(pre[k], primes[k] % ql, ql);
+    uint64_t inv_run = host_invmod(pre[L], ql);  // (prod_{l < j < L} q_j)^-1
+    for (uint32_t k = L - 1; k > l; --k) {
+      const uint64_t inv = host_mulmod(inv_run, pre[k], ql);  // q_k^-1
+      inv_run = host_mulmod(inv_run, primes[k] % ql, ql);
+      RescaleC& c = (*out)[rescale_index(k, l)];
+      c.inv = inv;
+      c.inv_shoup = (uint64_t)(((u128)inv << 64) / ql);
+      c.m = ql * ((primes[k] + ql - 1) / ql);
+      c.half = (primes[k] / 2) % ql;
+    }
+  }
+  return NTT_OK;
 }
 
 template <class T>
@@ -266,6 +296,11 @@ extern "C" int ntt_plan_create(ntt_plan** out, uint32_t n, const uint64_t* prime
     if (rc == NTT_OK) rc = upload(&p->d_fwd32, fwd32.data(), tn * sizeof(Narrow::Tw));
     if (rc == NTT_OK) rc = upload(&p->d_inv32, inv32.data(), tn * sizeof(Narrow::Tw));
     if (rc == NTT_OK) rc = upload(&p->d_mods, p->h_mods.data(), num_primes * sizeof(ModInfo));
+    if (rc == NTT_OK && num_primes > 1) {
+      std::vector<RescaleC> tri;
+      rc = rescale_triangle(primes, num_primes, &tri);
+      if (rc == NTT_OK) rc = upload(&p->d_rescale, tri.data(), tri.size() * sizeof(RescaleC));
+    }
     if (rc != NTT_OK) {
       free_device(p);
       delete p;
