@@ -46,6 +46,7 @@ def lib():
             "orc_crt_words": (i32, [_U64P, _U64P, u32, _U64P, u32]),
             "orc_relinearize": (i32, [_U64P, _U64P, _U64P, u64, u64, _U64P, u32, u32, u32, i32]),
             "orc_rescale": (i32, [_U64P, _U64P, i32, u64, u32, u64, _U64P]),
+            "orc_keyswitch_hoisted": (i32, [_U64P, _U64P, _U64P, _U64P, u32, u64, u64, _U64P, u32, u32, u32, i32]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -221,6 +222,23 @@ def keyswitch(ct, ksk, g: int, qp, nq: int, dnum: int, threads: int = 0) -> np.n
                              threads or default_threads())
     if rc:
         raise ValueError("bad key-switch arguments")
+    return out
+
+
+def keyswitch_hoisted(ct, ksk, gs, qp, nq: int, dnum: int, threads: int = 0) -> np.ndarray:
+    """ct: [batch, 2, nq, n]; ksk: [R, dnum, 2, nq+np, n]; gs: R elements -> [R, batch, 2, nq, n]."""
+    ct, ksk = _u64(ct), _u64(ksk)
+    n = ct.shape[-1]
+    assert ct.ndim == 4 and ct.shape[1:3] == (2, nq)
+    batch = ct.shape[0]
+    R = len(gs)
+    np_ = len(qp) - nq
+    assert ksk.shape == (R, dnum, 2, nq + np_, n), ksk.shape
+    out = np.zeros((R, batch, 2, nq, n), dtype=np.uint64)
+    rc = lib().orc_keyswitch_hoisted(_p(out), _p(ct), _p(ksk), _p(_u64(gs)), R, batch, n, _p(_u64(qp)), nq, np_,
+                                     dnum, threads or default_threads())
+    if rc:
+        raise ValueError("bad hoisted key-switch arguments")
     return out
 
 

@@ -619,6 +619,67 @@ int orc_keyswitch(uint64_t *out, const uint64_t *ct, const uint64_t *ksk, uint64
   return rc;
 }
 
+/* ---- hoisted rotations ------------------------------------------------------ */
+
+int orc_keyswitch_hoisted(uint64_t *out, const uint64_t *ct, const uint64_t *ksk, const uint64_t *gs, uint32_t R,
+                          uint64_t batch, uint64_t n, const uint64_t *qp, uint32_t nq, uint32_t np, uint32_t dnum,
+                          int threads) {
+  if (dnum == 0 || nq == 0 || nq % dnum != 0 || R == 0) return -1;
+  for (uint32_t r = 0; r < R; ++r)
+    if ((gs[r] & 1) == 0) return -1;
+  uint32_t nqp = nq + np, alpha = nq / dnum;
+  uint64_t plane = (uint64_t)nq * n, qplane = (uint64_t)nqp * n;
+  uint64_t *ext = (uint64_t *)malloc((uint64_t)dnum * qplane * sizeof(uint64_t));
+  uint64_t *perm = (uint64_t *)malloc((uint64_t)dnum * qplane * sizeof(uint64_t));
+  uint64_t *acc = (uint64_t *)malloc(2 * qplane * sizeof(uint64_t));
+  uint64_t *md = (uint64_t *)malloc(plane * sizeof(uint64_t));
+  uint64_t *c0r = (uint64_t *)malloc(plane * sizeof(uint64_t));
+  int rc = 0;
+  for (uint64_t bi = 0; bi < batch && rc == 0; ++bi) {
+    const uint64_t *c0 = ct + bi * 2 * plane, *c1 = c0 + plane;
+    /* decompose c1 (no automorphism) and extend every digit onto Q u P, then NTT */
+    for (uint32_t j = 0; j < dnum; ++j)
+      basis_extend_threads(c1 + (uint64_t)j * alpha * n, alpha, qp + (uint64_t)j * alpha, ext + (uint64_t)j * qplane,
+                           nqp, qp, n, threads);
+    if (orc_batch_ntt(ext, dnum, nqp, n, qp, 0, threads)) rc = -1;
+    for (uint32_t r = 0; r < R && rc == 0; ++r) {
+      const uint64_t g = gs[r];
+      const uint64_t *k = ksk + (uint64_t)r * dnum * 2 * qplane;
+      uint64_t *o = out + (r * batch + bi) * 2 * plane;
+      /* the automorphism of every extended digit, in the NTT domain */
+      for (uint64_t row = 0; row < (uint64_t)dnum * nqp; ++row) orc_automorph_ntt(ext + row * n, perm + row * n, n, g);
+      for (int comp = 0; comp < 2; ++comp)
+        for (uint32_t t = 0; t < nqp; ++t) {
+          uint64_t q = qp[t];
+          uint64_t *a = acc + ((uint64_t)comp * nqp + t) * n;
+          for (uint64_t e = 0; e < n; ++e) {
+            uint64_t s = 0;
+            for (uint32_t j = 0; j < dnum; ++j)
+              s = addm(s, mulm(perm[((uint64_t)j * nqp + t) * n + e], k[(((uint64_t)j * 2 + comp) * nqp + t) * n + e], q),
+                       q);
+            a[e] = s;
+          }
+        }
+      if (orc_batch_ntt(acc, 2, nqp, n, qp, 1, threads)) rc = -1;
+      for (uint32_t l = 0; l < nq; ++l) orc_automorph_coeff(c0 + (uint64_t)l * n, c0r + (uint64_t)l * n, n, qp[l], g);
+      for (int comp = 0; comp < 2; ++comp) {
+        moddown_threads(acc + (uint64_t)comp * qplane, md, qp, nq, np, n, threads);
+        for (uint32_t l = 0; l < nq; ++l)
+          for (uint64_t e = 0; e < n; ++e) {
+            uint64_t i = (uint64_t)l * n + e;
+            o[comp * plane + i] = comp == 0 ? addm(c0r[i], md[i], qp[l]) : md[i];
+          }
+      }
+    }
+  }
+  free(ext);
+  free(perm);
+  free(acc);
+  free(md);
+  free(c0r);
+  return rc;
+}
+
 /* ---- relinearisation -------------------------------------------------------- */
 
 int orc_relinearize(uint64_t *out, const uint64_t *d, const uint64_t *rlk, uint64_t batch, uint64_t n,

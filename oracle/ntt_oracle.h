@@ -122,6 +122,25 @@ void orc_moddown(const uint64_t *acc, uint64_t *out, const uint64_t *qp, uint32_
 int orc_keyswitch(uint64_t *out, const uint64_t *ct, const uint64_t *ksk, uint64_t g, uint64_t batch,
                   uint64_t n, const uint64_t *qp, uint32_t nq, uint32_t np, uint32_t dnum, int threads);
 
+/* Hoisted rotations: R Galois elements share one decomposition of c1 (the
+ * rotate_k / conj_extract / coeff_to_slot stages of the kestrel-llm overview,
+ * section 4.2, apply many rotations, and the conjugation g = 2n - 1, to one
+ * ciphertext).
+ *  ct:  [batch][2][nq][n] coefficient domain;  gs: R odd Galois elements < 2n;
+ *  ksk: [R][dnum][2][nq+np][n] NTT domain (key r carries sigma_{g_r}(s) to s);
+ *  out: [R][batch][2][nq][n].
+ *  Steps: digits of c1 WITHOUT the automorphism, exact CRT lift, reduced onto Q u P;
+ *  NTT of every extended digit (once); then for each r: the NTT-domain automorphism
+ *  of every extended limb (the slot permutation of orc_automorph_ntt), the inner
+ *  product with ksk[r], INTT, ModDown (exact floor), and sigma_{g_r}(c0) added to
+ *  component 0.  The digits are then sigma_g of the lifted integers, which differ
+ *  from the lifts of sigma_g(c1) where a coefficient changes sign; both are valid
+ *  decompositions (same congruence, same size bound), so this is its own result,
+ *  not orc_keyswitch's.  Returns 0, or -1 on a bad argument. */
+int orc_keyswitch_hoisted(uint64_t *out, const uint64_t *ct, const uint64_t *ksk, const uint64_t *gs, uint32_t R,
+                          uint64_t batch, uint64_t n, const uint64_t *qp, uint32_t nq, uint32_t np, uint32_t dnum,
+                          int threads);
+
 /* Relinearisation of a batch of tensor products d = (d0, d1, d2), each
  * [batch][3][nq][n] in the coefficient domain: the quadratic term is switched with
  * the relinearisation key rlk [dnum][2][nq+np][n] (NTT domain over Q u P), with no

@@ -624,3 +624,67 @@ def test_ciphertext_product_decrypts_to_the_scaled_product(ks_primes):
     # and encryption noise are far below one unit after the division by q_last
     assert worst < n / 2 + 2, worst
     assert any(uu)
+
+
+# ---- P13: hoisted rotations -----------------------------------------------------------
+
+def test_hoisted_identity_rotation_equals_keyswitch(ks_primes):
+    """With g = 1 there is no automorphism, so sharing the decomposition changes nothing."""
+    Q, P = ks_primes
+    qp = list(Q) + list(P)
+    n = 256
+    ct = inputs.uniform_residues((2, 2, 24, n), Q, 1300)
+    ksk = inputs.uniform_residues((1, 3, 2, 32, n), qp, 1301)
+    got = orc.keyswitch_hoisted(ct, ksk, [1], qp, 24, 3)
+    assert np.array_equal(got[0], orc.keyswitch(ct, ksk[0], 1, qp, 24, 3))
+
+
+def test_hoisted_matches_coefficient_domain_route(ks_primes):
+    """The NTT-domain slot permutation of the shared digits equals the other route:
+    lift each digit, apply sigma_g to the lifted integer polynomial in the
+    coefficient domain (limb by limb over Q u P), then NTT; key product, INTT,
+    ModDown and sigma_g(c0) as in the key-switch definition."""
+    Q, P = ks_primes
+    qp = list(Q) + list(P)
+    n, dnum, alpha = 128, 3, 8
+    gs = [5, 25, 2 * n - 1]
+    ct = inputs.uniform_residues((1, 2, 24, n), Q, 1310)
+    ksk = inputs.uniform_residues((len(gs), dnum, 2, 32, n), qp, 1311)
+    got = orc.keyswitch_hoisted(ct, ksk, gs, qp, 24, dnum)
+    lifted = [orc.basis_extend(ct[0, 1, j * alpha:(j + 1) * alpha], Q[j * alpha:(j + 1) * alpha], qp)
+              for j in range(dnum)]
+    for r, g in enumerate(gs):
+        acc = np.zeros((2, 32, n), dtype=object)
+        for j in range(dnum):
+            dig = orc.batch_ntt(orc.batch_automorph(lifted[j], g, 0, qp), qp)
+            for c in range(2):
+                acc[c] += dig.astype(object) * ksk[r, j, c].astype(object)
+        qcol = np.array(qp, dtype=object)[:, None]
+        acc = (acc % qcol).astype(np.uint64)
+        coef = orc.batch_ntt(acc, qp, inverse=True)
+        c0r = orc.batch_automorph(ct[0, 0], g, 0, Q)
+        want0 = (orc.moddown(coef[0], qp, 24).astype(object) + c0r.astype(object)) % np.array(Q, dtype=object)[:, None]
+        assert np.array_equal(got[r, 0, 0], want0.astype(np.uint64)), g
+        assert np.array_equal(got[r, 0, 1], orc.moddown(coef[1], qp, 24)), g
+
+
+def test_hoisted_semantic_small_ring(ks_primes):
+    """Real rotation keys (including the conjugation 2n - 1) at n = 1024: output r
+    decrypts under s to what sigma_{g_r}(ct) decrypts to under sigma_{g_r}(s)."""
+    from tests import keygen
+    Q, P = ks_primes
+    qp = list(Q) + list(P)
+    n = 1024
+    gs = [5, 2 * n - 1, 25]
+    s = keygen.to_limbs(inputs.small_signed(n, 1, 1320), qp)
+    keys = np.stack([keygen.switching_key(orc.batch_automorph(s, g, 0, qp), s, qp, 24, 3, 1330 + 10 * i)
+                     for i, g in enumerate(gs)])
+    ct = inputs.uniform_residues((1, 2, 24, n), Q, 1340)
+    out = orc.keyswitch_hoisted(ct, keys, gs, qp, 24, 3)
+    sQ = s[:24]
+    for r, g in enumerate(gs):
+        lhs = keygen.padd(out[r, 0, 0], keygen.pmul(out[r, 0, 1], sQ, Q), Q)
+        c_rot = orc.batch_automorph(ct[0], g, 0, Q)
+        rhs = keygen.padd(c_rot[0], keygen.pmul(c_rot[1], orc.batch_automorph(sQ, g, 0, Q), Q), Q)
+        worst = keygen.centered_crt_max(keygen.psub(lhs, rhs, Q), Q, stride=7)
+        assert worst < (1 << 20), (g, worst)
