@@ -196,6 +196,32 @@ int keyswitch_workspace_size(const ntt_ks_plan *plan, uint64_t batch, size_t *by
 int keyswitch(const ntt_ks_plan *plan, uint64_t *out, const uint64_t *ct, const uint64_t *ksk,
               uint64_t galois_elt, uint64_t batch, void *workspace, size_t workspace_bytes, void *stream);
 
+/* Bytes of device workspace keyswitch_hoisted needs for num_rot rotations of `batch`
+ * ciphertexts: batch * (dnum + 2 num_rot) * (num_q + num_p) * n * 8. */
+int keyswitch_hoisted_workspace_size(const ntt_ks_plan *plan, uint32_t num_rot, uint64_t batch, size_t *bytes);
+
+/* Hoisted rotations: num_rot Galois elements applied to the same ciphertexts with
+ * ONE decomposition (ModUp and forward NTT of c1 once, then per rotation the
+ * NTT-domain automorphism of the shared digits -- a slot permutation fused into the
+ * key product -- INTT and ModDown).  The rotate_k, conj_extract (g = 2n - 1) and
+ * coeff_to_slot stages of the kestrel-llm overview, section 4.2, apply many
+ * rotations to one ciphertext.
+ *   ct          : [batch][2][num_q][n], coefficient domain;
+ *   ksk         : [num_rot][dnum][2][num_q + num_p][n], key r for galois_elts[r];
+ *   galois_elts : HOST array of num_rot odd elements < 2n (1 <= num_rot <= 64);
+ *   out         : [num_rot][batch][2][num_q][n];
+ *   out[r] = ( sigma_g(c0) + ModDown(acc_0), ModDown(acc_1) ),
+ *   acc_c = INTT( sum_j slot_g(NTT(ModUp(digit_j(c1)))) * ksk[r][j][c] ).
+ * The digits are sigma_g of the lifted digits of c1, not the lifts of
+ * sigma_g(c1): where sigma_g flips a coefficient's sign they differ by the digit
+ * modulus, so the result differs from keyswitch() by a valid re-encryption of the
+ * same value (both decompositions satisfy the same congruence and bound).
+ * dnum <= 16.  workspace: keyswitch_hoisted_workspace_size bytes, 256-byte
+ * aligned.  out must not overlap ct, ksk or workspace. */
+int keyswitch_hoisted(const ntt_ks_plan *plan, uint64_t *out, const uint64_t *ct, const uint64_t *ksk,
+                      const uint64_t *galois_elts, uint32_t num_rot, uint64_t batch, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
 /* Relinearisation of tensor products (the "relin" operation of the kestrel-llm
  * overview's CKKS layer, section 3; it closes the ciphertext-ciphertext multiply
  * whose tensor step is ct_tensor_ntt):

@@ -55,6 +55,8 @@ def lib():
             "keyswitch": (i32, [_VP, _VP, _VP, _VP, u64, u64, _VP, sz, _VP]),
             "keyswitch_plan_destroy": (None, [_VP]),
             "relinearize": (i32, [_VP, _VP, _VP, _VP, u64, _VP, sz, _VP]),
+            "keyswitch_hoisted_workspace_size": (i32, [_VP, u32, u64, ctypes.POINTER(sz)]),
+            "keyswitch_hoisted": (i32, [_VP, _VP, _VP, _VP, _U64P, u32, u64, _VP, sz, _VP]),
             "rescale": (i32, [_VP, _VP, _VP, i32, u64, u32, u32, _VP]),
         }
         for name, (res, args) in sig.items():
@@ -286,6 +288,37 @@ def keyswitch(ks: KeySwitchPlan, out, ct, ksk, galois_elt: int, ws=None, stream=
     _check(lib().keyswitch(ks.handle, _VP(out.data_ptr()), _VP(ct.data_ptr()), _VP(ksk.data_ptr()), galois_elt,
                            batch, _VP(ws.data_ptr()), ws.numel() * ws.element_size(), _stream_ptr(ct, stream)),
            "keyswitch")
+    return out
+
+
+def hoisted_workspace(ks: KeySwitchPlan, num_rot: int, batch: int = 1):
+    """A device workspace (uint8) for keyswitch_hoisted with num_rot rotations of `batch` ciphertexts."""
+    import torch
+    v = ctypes.c_size_t()
+    _check(lib().keyswitch_hoisted_workspace_size(ks.handle, num_rot, batch, ctypes.byref(v)),
+           "keyswitch_hoisted_workspace_size")
+    return torch.empty(max(int(v.value), 1), dtype=torch.uint8, device=f"cuda:{ks.qp_plan.device}")
+
+
+def keyswitch_hoisted(ks: KeySwitchPlan, out, ct, ksk, galois_elts, ws=None, stream=None):
+    """Hoisted rotations; ct [batch, 2, num_q, n], ksk [R, dnum, 2, num_q + num_p, n] -> out [R, batch, 2, num_q, n]."""
+    plan = ks.qp_plan
+    batch, limbs = _check_tensor(ct, plan, "ct", lead=1)
+    _check_tensor(out, plan, "out", lead=1)
+    _check_tensor(ksk, plan, "ksk", lead=1)
+    R = len(galois_elts)
+    if limbs != ks.num_q or ct.dim() != 4 or ct.shape[1] != 2:
+        raise ValueError("ct must be [batch, 2, num_q, n]")
+    if tuple(out.shape) != (R,) + tuple(ct.shape):
+        raise ValueError("out must be [R, batch, 2, num_q, n]")
+    if tuple(ksk.shape) != (R, ks.dnum, 2, ks.num_q + ks.num_p, plan.n):
+        raise ValueError("ksk must be [R, dnum, 2, num_q + num_p, n]")
+    if ws is None:
+        ws = hoisted_workspace(ks, R, batch)
+    _gs_arr, gs_ptr = _u64arr(galois_elts)
+    _check(lib().keyswitch_hoisted(ks.handle, _VP(out.data_ptr()), _VP(ct.data_ptr()), _VP(ksk.data_ptr()),
+                                   gs_ptr, R, batch, _VP(ws.data_ptr()),
+                                   ws.numel() * ws.element_size(), _stream_ptr(ct, stream)), "keyswitch_hoisted")
     return out
 
 

@@ -199,6 +199,77 @@ __global__ __launch_bounds__(kKsThreads) void mac_kernel(uint64_t* __restrict__ 
   *reinterpret_cast<ulonglong2*>(o + plane) = s1;
 }
 
+// ---- key inner product for hoisted rotations -------------------------------------------
+// The NTT-domain automorphism in bit-reversed slot order: out[k] = in[slot(k)] with
+// 2 brv(slot) + 1 = (2 brv(k) + 1) g mod 2n, i.e. brv(slot) = g brv(k) + (g - 1) / 2
+// mod n.  It maps every aligned segment of 2^m slots onto an aligned segment: the
+// low log n - m bits of g brv(k) + c depend only on those of brv(k), which are the
+// reversed high bits of k, fixed inside the segment.
+__device__ __forceinline__ uint32_t ntt_slot(uint32_t k, uint32_t g, uint32_t logn) {
+  const uint32_t K = __brev(k) >> (32 - logn);
+  const uint32_t P = (uint32_t)(((uint64_t)K * g + (g >> 1)) & ((1u << logn) - 1));
+  return __brev(P) >> (32 - logn);
+}
+
+constexpr uint32_t kMaxHoisted = 64;
+struct HoistArgs {
+  uint32_t g[kMaxHoisted];  // Galois elements
+  uint32_t h[kMaxHoisted];  // their inverses mod 2n
+};
+
+// One block owns an aligned segment S of one limb of the NTT-domain digits and stages
+// it in LDS for all dnum digits; for rotation r it then produces the output segment
+// slot_r^-1(S) = slot_{h_r}(S), reading the key and writing the accumulators with
+// coalesced 16-byte accesses and gathering the digits from LDS.  The digits are read
+// from HBM once for all R rotations.
+// grid.x: nseg * nqp; grid.y: batch.  acc: [R][batch][2][nqp][n].
+__global__ __launch_bounds__(kKsThreads) void mac_hoisted_kernel(uint64_t* __restrict__ acc,
+                                                                 const uint64_t* __restrict__ ext,
+                                                                 const uint64_t* __restrict__ ksk,
+                                                                 const ModInfo* __restrict__ mods, uint32_t logn,
+                                                                 uint32_t seglog, uint32_t nqp, uint32_t dnum,
+                                                                 uint32_t R, uint32_t batch, HoistArgs ha) {
+  extern __shared__ uint64_t seg_lds[];  // [dnum][seg]
+  const uint32_t seg = 1u << seglog, nseg = 1u << (logn - seglog);
+  const uint32_t t = blockIdx.x >> (logn - seglog), s0 = (blockIdx.x & (nseg - 1)) << seglog;
+  const uint32_t b = blockIdx.y;
+  const uint64_t plane = (uint64_t)nqp << logn;
+  const uint64_t row = (uint64_t)t << logn;
+  const uint32_t i2 = 2 * threadIdx.x;
+  const bool active = i2 < seg;
+  if (active) {
+    const uint64_t* xe = ext + (uint64_t)b * dnum * plane + row + s0 + i2;
+    for (uint32_t j = 0; j < dnum; ++j) {
+      const ulonglong2 v = *reinterpret_cast<const ulonglong2*>(xe + (uint64_t)j * plane);
+      seg_lds[j * seg + i2] = v.x;
+      seg_lds[j * seg + i2 + 1] = v.y;
+    }
+  }
+  __syncthreads();
+  if (!active) return;
+  const Barrett br = mods[t].br;
+  const uint64_t q = br.q;
+  for (uint32_t r = 0; r < R; ++r) {
+    const uint32_t g = ha.g[r];
+    const uint32_t k0 = (ntt_slot(s0, ha.h[r], logn) & ~(seg - 1)) + i2;
+    const uint32_t p0 = ntt_slot(k0, g, logn) - s0, p1 = ntt_slot(k0 + 1, g, logn) - s0;
+    const uint64_t* kr = ksk + (uint64_t)r * dnum * 2 * plane + row + k0;
+    ulonglong2 a0 = {0, 0}, a1 = {0, 0};
+    for (uint32_t j = 0; j < dnum; ++j) {
+      const uint64_t d0 = seg_lds[j * seg + p0], d1 = seg_lds[j * seg + p1];
+      const ulonglong2 k0v = *reinterpret_cast<const ulonglong2*>(kr + (uint64_t)(2 * j) * plane);
+      const ulonglong2 k1v = *reinterpret_cast<const ulonglong2*>(kr + (uint64_t)(2 * j + 1) * plane);
+      a0.x = add_mod(a0.x, barrett_mul(d0, k0v.x, br), q);
+      a0.y = add_mod(a0.y, barrett_mul(d1, k0v.y, br), q);
+      a1.x = add_mod(a1.x, barrett_mul(d0, k1v.x, br), q);
+      a1.y = add_mod(a1.y, barrett_mul(d1, k1v.y, br), q);
+    }
+    uint64_t* o = acc + ((uint64_t)r * batch + b) * 2 * plane + row + k0;
+    *reinterpret_cast<ulonglong2*>(o) = a0;
+    *reinterpret_cast<ulonglong2*>(o + plane) = a1;
+  }
+}
+
 // ---- ModDown + the additive part -----------------------------------------------------
 // grid.x: coefficient tiles; grid.y: batch * 2 (component); grid.z: groups of the nq
 // output primes (the Garner digits over P are recomputed per group).
@@ -424,22 +495,14 @@ void launch_moddown(dim3 grid, hipStream_t s, uint64_t* out, const uint64_t* acc
                      io.add_mask, p->dev, p->qp->logn, h, p->nq, p->np);
 }
 
-// The five launches of one key-switch (arguments validated).  grid.y carries batch x
-// digits (ModUp) and batch x 2 (ModDown); a batch whose product would exceed the
-// grid's y range is split into chunks.
-int ks_run(const ntt_ks_plan* p, uint64_t* out, const KsIo& io, const uint64_t* ksk, uint64_t galois_elt,
-           uint64_t batch, void* workspace, hipStream_t s) {
-  const ntt_plan* qp = p->qp;
-  const uint32_t n = qp->n, nq = p->nq, nqp = nq + p->np, dnum = p->dnum;
-  DeviceGuard g(qp->device);
-  if (!g.ok) return NTT_EDEVICE;
-  uint64_t* ext = (uint64_t*)workspace;
-  uint64_t* acc = ext + batch * (uint64_t)dnum * nqp * n;
-  const uint32_t two_n = 2 * n;
-  const uint32_t h = (uint32_t)host_invmod(galois_elt % two_n, two_n);
-  const uint32_t tiles = (n + kKsThreads - 1) / kKsThreads;
-  constexpr uint64_t kMaxGridY = 65535;
+constexpr uint64_t kMaxGridY = 65535;
 
+// ModUp of `batch` inputs into ext [batch][dnum][nqp][n] (sigma_h gathered on load).
+// grid.y carries batch x digits; a batch whose product exceeds the grid's y range is
+// split into chunks.
+int ks_modup(const ntt_ks_plan* p, uint64_t* ext, const KsIo& io, uint32_t h, uint64_t batch, hipStream_t s) {
+  const uint32_t n = p->qp->n, nqp = p->nq + p->np, dnum = p->dnum;
+  const uint32_t tiles = (n + kKsThreads - 1) / kKsThreads;
   // Groups of target primes per coefficient: enough resident waves to hide the
   // latency of the long dependent Shoup chains (measured on MI355X).
   const uint32_t up_groups = std::max(1u, std::min(kModUpGroups, nqp - p->alpha));
@@ -459,16 +522,15 @@ int ks_run(const ntt_ks_plan* p, uint64_t* out, const KsIo& io, const uint64_t* 
     }
     if (hipGetLastError() != hipSuccess) return NTT_EDEVICE;
   }
-  if (launch_ntt(qp, ext, batch * dnum, 0, nqp, false, s) != hipSuccess) return NTT_EDEVICE;
-  const uint64_t pairs = (uint64_t)nqp * n / 2;
-  for (uint64_t b0 = 0; b0 < batch; b0 += kMaxGridY) {
-    const uint64_t nb = std::min(kMaxGridY, batch - b0);
-    hipLaunchKernelGGL(mac_kernel, dim3((uint32_t)((pairs + kKsThreads - 1) / kKsThreads), (uint32_t)nb),
-                       dim3(kKsThreads), 0, s, acc + b0 * 2 * nqp * n, ext + b0 * dnum * nqp * n, ksk, qp->d_mods,
-                       qp->logn, nqp, dnum, pairs);
-    if (hipGetLastError() != hipSuccess) return NTT_EDEVICE;
-  }
-  if (launch_ntt(qp, acc, batch * 2, 0, nqp, true, s) != hipSuccess) return NTT_EDEVICE;
+  return NTT_OK;
+}
+
+// ModDown of acc [batch][2][nqp][n] into out [batch][2][nq][n], adding the sigma_h
+// gathered additive inputs selected by io.add_mask.
+int ks_moddown(const ntt_ks_plan* p, uint64_t* out, const uint64_t* acc, const KsIo& io, uint32_t h, uint64_t batch,
+               hipStream_t s) {
+  const uint32_t n = p->qp->n, nq = p->nq, nqp = nq + p->np;
+  const uint32_t tiles = (n + kKsThreads - 1) / kKsThreads;
   const uint32_t down_groups = std::max(1u, std::min(kModDownGroups, nq));
   const uint64_t down_chunk = kMaxGridY / 2;
   for (uint64_t b0 = 0; b0 < batch; b0 += down_chunk) {
@@ -488,6 +550,36 @@ int ks_run(const ntt_ks_plan* p, uint64_t* out, const KsIo& io, const uint64_t* 
     if (hipGetLastError() != hipSuccess) return NTT_EDEVICE;
   }
   return NTT_OK;
+}
+
+uint32_t galois_inverse(const ntt_plan* qp, uint64_t g) {
+  const uint32_t two_n = 2 * qp->n;
+  return (uint32_t)host_invmod(g % two_n, two_n);
+}
+
+// The five launches of one key-switch (arguments validated).
+int ks_run(const ntt_ks_plan* p, uint64_t* out, const KsIo& io, const uint64_t* ksk, uint64_t galois_elt,
+           uint64_t batch, void* workspace, hipStream_t s) {
+  const ntt_plan* qp = p->qp;
+  const uint32_t n = qp->n, nqp = p->nq + p->np, dnum = p->dnum;
+  DeviceGuard g(qp->device);
+  if (!g.ok) return NTT_EDEVICE;
+  uint64_t* ext = (uint64_t*)workspace;
+  uint64_t* acc = ext + batch * (uint64_t)dnum * nqp * n;
+  const uint32_t h = galois_inverse(qp, galois_elt);
+  int rc = ks_modup(p, ext, io, h, batch, s);
+  if (rc) return rc;
+  if (launch_ntt(qp, ext, batch * dnum, 0, nqp, false, s) != hipSuccess) return NTT_EDEVICE;
+  const uint64_t pairs = (uint64_t)nqp * n / 2;
+  for (uint64_t b0 = 0; b0 < batch; b0 += kMaxGridY) {
+    const uint64_t nb = std::min(kMaxGridY, batch - b0);
+    hipLaunchKernelGGL(mac_kernel, dim3((uint32_t)((pairs + kKsThreads - 1) / kKsThreads), (uint32_t)nb),
+                       dim3(kKsThreads), 0, s, acc + b0 * 2 * nqp * n, ext + b0 * dnum * nqp * n, ksk, qp->d_mods,
+                       qp->logn, nqp, dnum, pairs);
+    if (hipGetLastError() != hipSuccess) return NTT_EDEVICE;
+  }
+  if (launch_ntt(qp, acc, batch * 2, 0, nqp, true, s) != hipSuccess) return NTT_EDEVICE;
+  return ks_moddown(p, out, acc, io, h, batch, s);
 }
 }  // namespace
 
@@ -514,6 +606,67 @@ extern "C" int relinearize(const ntt_ks_plan* p, uint64_t* out, const uint64_t* 
   const int rc = ks_check(p, out, io, rlk, batch, workspace, workspace_bytes);
   if (rc) return rc;
   return ks_run(p, out, io, rlk, 1, batch, workspace, (hipStream_t)stream);
+}
+
+extern "C" int keyswitch_hoisted_workspace_size(const ntt_ks_plan* p, uint32_t num_rot, uint64_t batch,
+                                               size_t* bytes) {
+  if (!p || !bytes || num_rot == 0) return NTT_EINVAL;
+  if (batch > 4096 || num_rot > kMaxHoisted) return NTT_EUNSUPPORTED;
+  const uint64_t qplane = (uint64_t)(p->nq + p->np) * p->qp->n;
+  *bytes = (size_t)(batch * (p->dnum + 2ull * num_rot) * qplane * 8);
+  return NTT_OK;
+}
+
+extern "C" int keyswitch_hoisted(const ntt_ks_plan* p, uint64_t* out, const uint64_t* ct, const uint64_t* ksk,
+                                 const uint64_t* galois_elts, uint32_t num_rot, uint64_t batch, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  if (!p || !galois_elts || num_rot == 0) return NTT_EINVAL;
+  const ntt_plan* qp = p->qp;
+  const uint32_t n = qp->n, nq = p->nq, nqp = nq + p->np, dnum = p->dnum;
+  if (num_rot > kMaxHoisted || batch > 4096) return NTT_EUNSUPPORTED;
+  if (dnum > 16) return NTT_EUNSUPPORTED;  // the digits of one segment are staged in LDS
+  for (uint32_t r = 0; r < num_rot; ++r)
+    if (!(galois_elts[r] & 1) || galois_elts[r] >= 2ull * n) return NTT_EINVAL;
+  if (batch == 0) return NTT_OK;
+  if (!out || !ct || !ksk || !workspace) return NTT_EINVAL;
+  if (((uintptr_t)out | (uintptr_t)ct | (uintptr_t)ksk) & 15u) return NTT_EINVAL;
+  if ((uintptr_t)workspace & 255u) return NTT_EINVAL;
+  const uint64_t plane = (uint64_t)nq * n, qplane = (uint64_t)nqp * n;
+  const uint64_t need = batch * (dnum + 2ull * num_rot) * qplane * 8;
+  if (workspace_bytes < need) return NTT_EINVAL;
+  const uint64_t ct_bytes = batch * 2 * plane * 8, out_bytes = num_rot * ct_bytes;
+  const uint64_t ksk_bytes = (uint64_t)num_rot * dnum * 2 * qplane * 8;
+  if (ranges_overlap(out, out_bytes, ct, ct_bytes) || ranges_overlap(out, out_bytes, ksk, ksk_bytes) ||
+      ranges_overlap(out, out_bytes, workspace, need) || ranges_overlap(workspace, need, ct, ct_bytes) ||
+      ranges_overlap(workspace, need, ksk, ksk_bytes))
+    return NTT_EOVERLAP;
+
+  DeviceGuard g(qp->device);
+  if (!g.ok) return NTT_EDEVICE;
+  hipStream_t s = (hipStream_t)stream;
+  HoistArgs ha{};
+  for (uint32_t r = 0; r < num_rot; ++r) {
+    ha.g[r] = (uint32_t)galois_elts[r];
+    ha.h[r] = galois_inverse(qp, galois_elts[r]);
+  }
+  uint64_t* ext = (uint64_t*)workspace;
+  uint64_t* acc = ext + batch * (uint64_t)dnum * qplane;
+  const KsIo io{ct + plane, 2 * plane, ct, 2 * plane, 1u, ct_bytes, ct};
+  int rc = ks_modup(p, ext, io, 1, batch, s);  // no automorphism: the digits are shared
+  if (rc) return rc;
+  if (launch_ntt(qp, ext, batch * dnum, 0, nqp, false, s) != hipSuccess) return NTT_EDEVICE;
+  const uint32_t seglog = std::min(qp->logn, 9u);
+  const dim3 grid((nqp << (qp->logn - seglog)), (uint32_t)batch);
+  hipLaunchKernelGGL(mac_hoisted_kernel, grid, dim3(kKsThreads), (size_t)dnum * (8u << seglog), s, acc, ext, ksk,
+                     qp->d_mods, qp->logn, seglog, nqp, dnum, num_rot, (uint32_t)batch, ha);
+  if (hipGetLastError() != hipSuccess) return NTT_EDEVICE;
+  if (launch_ntt(qp, acc, batch * 2 * num_rot, 0, nqp, true, s) != hipSuccess) return NTT_EDEVICE;
+  for (uint32_t r = 0; r < num_rot; ++r) {
+    rc = ks_moddown(p, out + (uint64_t)r * batch * 2 * plane, acc + (uint64_t)r * batch * 2 * qplane, io, ha.h[r],
+                    batch, s);
+    if (rc) return rc;
+  }
+  return NTT_OK;
 }
 
 extern "C" void keyswitch_plan_destroy(ntt_ks_plan* p) {

@@ -197,3 +197,78 @@ def test_ciphertext_product_pipeline_vs_oracle(B):
     dd = orc.batch_ntt(orc.batch_tensor(fa, fb, Q), Q, inverse=True)
     want = orc.rescale(orc.relinearize(dd, rlk, qp, 24, 3), Q, 1)
     assert_bits_equal(got, want, "ciphertext product pipeline")
+
+
+# ---- hoisted rotations ------------------------------------------------------------------
+
+def _hoisted_gpu(B, ks, ct, ksk, gs):
+    R = len(gs)
+    out = dev(np.zeros((R,) + ct.shape, dtype=np.uint64))
+    return host(B.keyswitch_hoisted(ks, out, dev(ct), dev(ksk), gs))
+
+
+def test_hoisted_workload_vs_oracle(B):
+    """The large-ring key-switch configuration with four rotations sharing one
+    decomposition: two powers of 5, the conjugation 2n - 1 and g = 1."""
+    w = workloads.KEYSWITCH
+    qp, plan, ks = _ks_setup(B, w.n)
+    gs = [5, 25, 2 * w.n - 1, 1]
+    ct = residues(w.shape_a, qp[:24], w.seed_a + 11)
+    ksk = residues((len(gs), 3, 2, 32, w.n), qp, w.seed_b + 11)
+    announce("hoisted workload", gs)
+    assert_bits_equal(_hoisted_gpu(B, ks, ct, ksk, gs), orc.keyswitch_hoisted(ct, ksk, gs, qp, 24, 3),
+                      "hoisted workload")
+
+
+@pytest.mark.parametrize("logn,nq,npr,dnum,batch", [(1, 4, 2, 2, 1), (4, 4, 3, 4, 2), (9, 6, 2, 3, 2),
+                                                    (10, 24, 8, 3, 2), (11, 16, 16, 16, 1), (12, 6, 2, 2, 3)])
+def test_hoisted_shapes_vs_oracle(B, logn, nq, npr, dnum, batch):
+    """Rings below, at and above the 512-slot segment, dnum up to the LDS limit of 16."""
+    n = 1 << logn
+    qp, plan, ks = _ks_setup(B, n, nq, npr, dnum)
+    gs = sorted({1, 3 % (2 * n), 5 % (2 * n), (2 * n - 1), (2 * n - 3) % (2 * n) or 1})
+    gs = [g for g in gs if g % 2 == 1]
+    ct = residues((batch, 2, nq, n), qp[:nq], 7800 + logn)
+    ksk = residues((len(gs), dnum, 2, nq + npr, n), qp[: nq + npr], 7900 + logn)
+    announce("hoisted shape", logn, nq, npr, dnum, batch, gs)
+    assert_bits_equal(_hoisted_gpu(B, ks, ct, ksk, gs),
+                      orc.keyswitch_hoisted(ct, ksk, gs, qp[: nq + npr], nq, dnum), "hoisted shape")
+
+
+def test_hoisted_identity_equals_keyswitch(B):
+    n = 1 << 12
+    qp, plan, ks = _ks_setup(B, n)
+    ct = residues((2, 2, 24, n), qp[:24], 8000)
+    ksk = residues((1, 3, 2, 32, n), qp, 8001)
+    announce("hoisted identity")
+    got = _hoisted_gpu(B, ks, ct, ksk, [1])
+    ref = host(B.keyswitch(ks, dev(np.zeros_like(ct)), dev(ct), dev(ksk[0]), 1))
+    assert_bits_equal(got[0], ref, "hoisted g=1 vs keyswitch")
+
+
+def test_hoisted_validation(B):
+    import ctypes
+    import torch
+    n = 1 << 10
+    qp, plan, ks = _ks_setup(B, n)
+    L = B.lib()
+    ct = torch.zeros((1, 2, 24, n), dtype=torch.int64, device="cuda:0")
+    out = torch.zeros((2, 1, 2, 24, n), dtype=torch.int64, device="cuda:0")
+    ksk = torch.zeros((2, 3, 2, 32, n), dtype=torch.int64, device="cuda:0")
+    ws = B.hoisted_workspace(ks, 2, 1)
+    V = ctypes.c_void_p
+    nb = ws.numel()
+
+    def call(gs, R=None, o=out, w=ws, nbytes=nb):
+        arr = np.asarray(gs, dtype=np.uint64)
+        return L.keyswitch_hoisted(ks.handle, V(o.data_ptr()), V(ct.data_ptr()), V(ksk.data_ptr()),
+                                   arr.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)), len(gs) if R is None else R,
+                                   1, V(w.data_ptr()), nbytes, None)
+    assert call([5, 25]) == B.NTT_OK
+    assert call([5, 4]) == B.NTT_EINVAL          # even element
+    assert call([5, 2 * n + 1]) == B.NTT_EINVAL  # beyond 2n
+    assert call([5, 25], R=0) == B.NTT_EINVAL
+    assert call([5] * 65) == B.NTT_EUNSUPPORTED
+    assert call([5, 25], nbytes=nb - 1) == B.NTT_EINVAL
+    assert call([5, 25], w=ct) == B.NTT_EOVERLAP
+    torch.cuda.synchronize()
