@@ -46,6 +46,7 @@ def lib():
             "orc_crt_words": (i32, [_U64P, _U64P, u32, _U64P, u32]),
             "orc_relinearize": (i32, [_U64P, _U64P, _U64P, u64, u64, _U64P, u32, u32, u32, i32]),
             "orc_rescale": (i32, [_U64P, _U64P, i32, u64, u32, u64, _U64P]),
+            "orc_modraise": (i32, [_U64P, _U64P, u64, u32, u32, u64, _U64P]),
             "orc_keyswitch_hoisted": (i32, [_U64P, _U64P, _U64P, _U64P, u32, u64, u64, _U64P, u32, u32, u32, i32]),
         }
         for name, (res, args) in sig.items():
@@ -279,4 +280,18 @@ def rescale(x, primes, mode: int) -> np.ndarray:
     rc = lib().orc_rescale(_p(out), _p(x), mode, batch, limbs, n, _p(_u64(primes)))
     if rc:
         raise ValueError("bad rescale arguments")
+    return out
+
+
+def modraise(x, primes_to, from_limbs: int) -> np.ndarray:
+    """x: [..., from_limbs, n] over primes_to[:from_limbs] -> [..., len(primes_to), n]."""
+    x = _u64(x)
+    n = x.shape[-1]
+    assert x.shape[-2] == from_limbs
+    to = len(primes_to)
+    batch = x.size // (from_limbs * n)
+    out = np.zeros(x.shape[:-2] + (to, n), dtype=np.uint64)
+    rc = lib().orc_modraise(_p(out), _p(x), batch, from_limbs, to, n, _p(_u64(primes_to)))
+    if rc:
+        raise ValueError("bad modraise arguments")
     return out

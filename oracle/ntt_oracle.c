@@ -729,3 +729,13 @@ int orc_rescale(uint64_t *out, const uint64_t *in, int mode, uint64_t batch, uin
   crt_basis_free(&b);
   return 0;
 }
+
+/* ---- modraise ---------------------------------------------------------------- */
+
+int orc_modraise(uint64_t *out, const uint64_t *in, uint64_t batch, uint32_t from, uint32_t to, uint64_t n,
+                 const uint64_t *primes) {
+  if (from == 0 || to <= from) return -1;
+  for (uint64_t bi = 0; bi < batch; ++bi)
+    orc_basis_extend(in + bi * from * n, from, primes, out + bi * to * n, to, primes, n);
+  return 0;
+}

@@ -161,6 +161,16 @@ int orc_relinearize(uint64_t *out, const uint64_t *d, const uint64_t *rlk, uint6
 int orc_rescale(uint64_t *out, const uint64_t *in, int mode, uint64_t batch, uint32_t limbs, uint64_t n,
                 const uint64_t *primes);
 
+/* ModRaise (the first stage of the kestrel-llm bootstrapping profile, section 4.2:
+ * a Garner extension raises the modulus chain back to the full chain).
+ * in: [batch][from][n] coefficient domain modulo primes[0..from); out:
+ * [batch][to][n] modulo primes[0..to), to > from: out[t] = X mod primes[t] with X the
+ * exact CRT value of the column in [0, prod_{i<from} primes[i]) (the unsigned
+ * representative that Garner's mixed-radix reconstruction yields).  The first
+ * `from` output limbs equal the input.  Returns 0, or -1 on a bad argument. */
+int orc_modraise(uint64_t *out, const uint64_t *in, uint64_t batch, uint32_t from, uint32_t to, uint64_t n,
+                 const uint64_t *primes);
+
 /* Multi-word CRT helper exposed for tests: value of residues x[0..k) modulo
  * m[0..k) as little-endian 64-bit words into out (capacity `words`).  Returns the
  * number of significant words, or -1 if it does not fit. */

@@ -688,3 +688,42 @@ def test_hoisted_semantic_small_ring(ks_primes):
         rhs = keygen.padd(c_rot[0], keygen.pmul(c_rot[1], orc.batch_automorph(sQ, g, 0, Q), Q), Q)
         worst = keygen.centered_crt_max(keygen.psub(lhs, rhs, Q), Q, stride=7)
         assert worst < (1 << 20), (g, worst)
+
+
+# ---- P14: modraise -------------------------------------------------------------------
+
+def test_modraise_closed_form(ks_primes):
+    """Columns with known integers X in [0, Q_from): every output limb is X mod q;
+    the input limbs are kept."""
+    Q, _ = ks_primes
+    ps = list(Q[:10])
+    frm = 3
+    Qf = 1
+    for q in ps[:frm]:
+        Qf *= q
+    rng = random.Random(1400)
+    xs = [0, 1, Qf - 1, Qf // 2, Qf // 2 + 1] + [rng.randrange(Qf) for _ in range(59)]
+    x = np.array([[v % q for v in xs] for q in ps[:frm]], dtype=np.uint64)[None]
+    out = orc.modraise(x, ps, frm)[0]
+    for t, q in enumerate(ps):
+        assert [int(v) for v in out[t]] == [v % q for v in xs]
+
+
+def test_modraise_decrypts_modulo_the_low_modulus(ks_primes):
+    """A level-1 ciphertext raised to 24 primes decrypts to m + e + q_0 I with a
+    small integer polynomial I (|I| <= ||s||_1 + 1); reducing that decryption
+    modulo q_0 gives back exactly the level-1 decryption."""
+    from tests import keygen
+    Q, _ = ks_primes
+    n = 256
+    q0 = Q[0]
+    s = keygen.to_limbs(inputs.small_signed(n, 1, 1410), Q)
+    m = keygen.to_limbs([(1 << 40) * v for v in inputs.small_signed(n, 5, 1411)], Q[:1])
+    ct = _ciphertext(m, s[:1], Q[:1], 1420)
+    low = keygen.centered_values(keygen.padd(ct[0], keygen.pmul(ct[1], s[:1], Q[:1]), Q[:1]), Q[:1])
+    up = orc.modraise(ct, Q, 1)
+    full = keygen.centered_values(keygen.padd(up[0], keygen.pmul(up[1], s, Q), Q), Q)
+    l1 = sum(abs(int(v)) for v in inputs.small_signed(n, 1, 1410))
+    for a, b in zip(full, low):
+        assert (a - b) % q0 == 0
+        assert abs((a - b) // q0) <= l1 + 1
