@@ -69,6 +69,7 @@ typedef enum {
 
 typedef struct ntt_plan ntt_plan;       /* opaque: n, primes, tables; immutable */
 typedef struct ntt_ks_plan ntt_ks_plan; /* opaque: key-switch constants; immutable */
+typedef struct ntt_mr_plan ntt_mr_plan; /* opaque: modraise constants; immutable */
 
 /* Human-readable name of a status code (static string). */
 const char *ntt_status_string(int status);
@@ -237,6 +238,25 @@ int relinearize(const ntt_ks_plan *plan, uint64_t *out, const uint64_t *d, const
                 void *workspace, size_t workspace_bytes, void *stream);
 
 void keyswitch_plan_destroy(ntt_ks_plan *plan);
+
+/* ---- ModRaise ------------------------------------------------------------ */
+
+/* ModRaise plan: lift from the first num_from primes of `plan` to its first num_to
+ * (num_from < num_to <= primes in plan, num_from <= 16).  Precomputes the Garner
+ * constants of the source primes and their products modulo every target.  `plan`
+ * must be a device plan and must outlive this plan. */
+int modraise_plan_create(ntt_mr_plan **out, const ntt_plan *plan, uint32_t num_from, uint32_t num_to);
+
+/* ModRaise, the first stage of the kestrel-llm bootstrapping profile (section 4.2:
+ * a Garner extension raises the modulus chain back to the full chain).
+ *   in  : [batch][num_from][n], coefficient domain;
+ *   out : [batch][num_to][n]: out[t] = X mod q_t with X in [0, q_0 ... q_{from-1})
+ *         the exact CRT value of the column (Garner's unsigned representative); the
+ *         first num_from limbs equal the input.
+ * out must not overlap in (NTT_EOVERLAP). */
+int modraise(const ntt_mr_plan *plan, uint64_t *out, const uint64_t *in, uint64_t batch, void *stream);
+
+void modraise_plan_destroy(ntt_mr_plan *plan);
 
 #ifdef __cplusplus
 }

@@ -55,6 +55,9 @@ def lib():
             "keyswitch": (i32, [_VP, _VP, _VP, _VP, u64, u64, _VP, sz, _VP]),
             "keyswitch_plan_destroy": (None, [_VP]),
             "relinearize": (i32, [_VP, _VP, _VP, _VP, u64, _VP, sz, _VP]),
+            "modraise_plan_create": (i32, [ctypes.POINTER(_VP), _VP, u32, u32]),
+            "modraise": (i32, [_VP, _VP, _VP, u64, _VP]),
+            "modraise_plan_destroy": (None, [_VP]),
             "keyswitch_hoisted_workspace_size": (i32, [_VP, u32, u64, ctypes.POINTER(sz)]),
             "keyswitch_hoisted": (i32, [_VP, _VP, _VP, _VP, _U64P, u32, u64, _VP, sz, _VP]),
             "rescale": (i32, [_VP, _VP, _VP, i32, u64, u32, u32, _VP]),
@@ -339,6 +342,45 @@ def relinearize(ks: KeySwitchPlan, out, d, rlk, ws=None, stream=None):
     _check(lib().relinearize(ks.handle, _VP(out.data_ptr()), _VP(d.data_ptr()), _VP(rlk.data_ptr()), batch,
                              _VP(ws.data_ptr()), ws.numel() * ws.element_size(), _stream_ptr(d, stream)),
            "relinearize")
+    return out
+
+
+class ModRaisePlan:
+    """Garner constants to lift from the first num_from primes of a plan to its first num_to."""
+
+    def __init__(self, plan: Plan, num_from: int, num_to: int):
+        self.plan = plan  # keeps the device tables alive
+        self.num_from, self.num_to = int(num_from), int(num_to)
+        h = _VP()
+        _check(lib().modraise_plan_create(ctypes.byref(h), plan.handle, num_from, num_to), "modraise_plan_create")
+        self._h = h
+
+    @property
+    def handle(self):
+        if self._h is None:
+            raise ValueError("plan destroyed")
+        return self._h
+
+    def destroy(self):
+        if getattr(self, "_h", None) is not None:
+            lib().modraise_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def modraise(mr: ModRaisePlan, out, x, stream=None):
+    """x [..., num_from, n] -> out [..., num_to, n] (exact lift onto the longer chain)."""
+    batch, limbs = _check_tensor(x, mr.plan, "x")
+    _check_tensor(out, mr.plan, "out")
+    if limbs != mr.num_from or tuple(out.shape) != tuple(x.shape[:-2]) + (mr.num_to, mr.plan.n):
+        raise ValueError("x must be [..., num_from, n] and out [..., num_to, n]")
+    _check(lib().modraise(mr.handle, _VP(out.data_ptr()), _VP(x.data_ptr()), batch, _stream_ptr(x, stream)),
+           "modraise")
     return out
 
 

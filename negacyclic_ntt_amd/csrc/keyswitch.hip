@@ -316,6 +316,46 @@ __global__ __launch_bounds__(kKsThreads) void moddown_kernel(uint64_t* __restric
   }
 }
 
+// ---- ModRaise ---------------------------------------------------------------------------
+// The exact Garner lift of each coefficient from the first `from` primes, reduced onto
+// primes from .. to-1 (the kestrel-llm bootstrapping profile's first stage).
+// grid.x: coefficient tiles; grid.y: batch; grid.z: groups of target primes.
+// in: [batch][from][n]; out: [batch][to][n].
+template <bool B60, int K>
+__global__ __launch_bounds__(kKsThreads) void modraise_kernel(uint64_t* __restrict__ out,
+                                                              const uint64_t* __restrict__ in,
+                                                              const uint64_t* __restrict__ moduli,
+                                                              const Tw* __restrict__ gar, const Tw* __restrict__ ev,
+                                                              uint32_t logn, uint32_t from, uint32_t to) {
+  const uint32_t n = 1u << logn;
+  const uint32_t e = blockIdx.x * kKsThreads + threadIdx.x;
+  if (e >= n) return;
+  const uint64_t* x_in = in + (uint64_t)blockIdx.y * from * n + e;
+  uint64_t* o = out + (uint64_t)blockIdx.y * to * n + e;
+  uint64_t x[K], v[K];
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    if (i >= (int)from) break;
+    x[i] = x_in[(uint64_t)i * n];
+  }
+  if (blockIdx.z == 0) {
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      if (i >= (int)from) break;
+      o[(uint64_t)i * n] = x[i];
+    }
+  }
+  constexpr int S = kMaxDigitPrimes;
+  garner<B60, K, S>(x, v, from, moduli, gar);
+  const uint32_t others = to - from, per = (others + gridDim.z - 1) / gridDim.z;
+  const uint32_t m0 = blockIdx.z * per, m1 = min(others, m0 + per);
+#pragma unroll 4
+  for (uint32_t m = m0; m < m1; ++m) {
+    const uint32_t t = from + m;
+    o[(uint64_t)t * n] = mixed_radix_eval<B60, K>(v, from, ev + (size_t)t * S, moduli[t]);
+  }
+}
+
 }  // namespace
 }  // namespace nntt
 
@@ -673,6 +713,117 @@ extern "C" void keyswitch_plan_destroy(ntt_ks_plan* p) {
   if (!p) return;
   if (p->d_const) {
     DeviceGuard g(p->qp->device);
+    (void)hipFree(p->d_const);
+  }
+  delete p;
+}
+
+// ---- ModRaise plan ----------------------------------------------------------------------
+
+struct ntt_mr_plan {
+  const ntt_plan* plan = nullptr;
+  uint32_t from = 0, to = 0;
+  bool below60 = false;
+  void* d_const = nullptr;
+  const uint64_t* moduli = nullptr;  // [to]
+  const Tw* garner = nullptr;        // [K][K] over the first `from` primes
+  const Tw* eval = nullptr;          // [to][K]
+};
+
+extern "C" int modraise_plan_create(ntt_mr_plan** out, const ntt_plan* plan, uint32_t from, uint32_t to) {
+  if (!out) return NTT_EINVAL;
+  *out = nullptr;
+  if (!plan) return NTT_EINVAL;
+  if (plan->device < 0) return NTT_EDEVICE;
+  if (from == 0 || to <= from || to > plan->num_primes) return NTT_EINVAL;
+  if (from > (uint32_t)kMaxDigitPrimes) return NTT_EUNSUPPORTED;
+  const uint32_t K = (uint32_t)kMaxDigitPrimes;
+  const uint64_t* m = plan->primes.data();
+  std::vector<Tw> gar((size_t)K * K, Tw{0, 0}), ev((size_t)to * K, Tw{0, 0});
+  garner_table(m, from, K, gar.data());
+  for (uint32_t t = 0; t < to; ++t) eval_table(m, from, m[t], ev.data() + (size_t)t * K);
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t sz_m = (size_t)to * 8, sz_g = gar.size() * sizeof(Tw), sz_e = ev.size() * sizeof(Tw);
+  const size_t total = al(sz_m) + al(sz_g) + al(sz_e);
+  std::vector<uint8_t> blob(total, 0);
+  memcpy(blob.data(), m, sz_m);
+  memcpy(blob.data() + al(sz_m), gar.data(), sz_g);
+  memcpy(blob.data() + al(sz_m) + al(sz_g), ev.data(), sz_e);
+  ntt_mr_plan* p = new (std::nothrow) ntt_mr_plan;
+  if (!p) return NTT_ENOMEM;
+  {
+    DeviceGuard g(plan->device);
+    if (!g.ok) {
+      delete p;
+      return NTT_EDEVICE;
+    }
+    if (hipMalloc(&p->d_const, total) != hipSuccess) {
+      delete p;
+      return NTT_ENOMEM;
+    }
+    if (hipMemcpy(p->d_const, blob.data(), total, hipMemcpyHostToDevice) != hipSuccess) {
+      (void)hipFree(p->d_const);
+      delete p;
+      return NTT_EDEVICE;
+    }
+  }
+  uint8_t* base = (uint8_t*)p->d_const;
+  p->plan = plan;
+  p->from = from;
+  p->to = to;
+  p->below60 = range_below60(plan, 0, to);
+  p->moduli = (const uint64_t*)base;
+  p->garner = (const Tw*)(base + al(sz_m));
+  p->eval = (const Tw*)(base + al(sz_m) + al(sz_g));
+  *out = p;
+  return NTT_OK;
+}
+
+extern "C" int modraise(const ntt_mr_plan* p, uint64_t* out, const uint64_t* in, uint64_t batch, void* stream) {
+  if (!p) return NTT_EINVAL;
+  const ntt_plan* plan = p->plan;
+  const uint32_t n = plan->n;
+  if (batch > (1ull << 36) / ((uint64_t)p->to * n)) return NTT_EUNSUPPORTED;
+  if (batch == 0) return NTT_OK;
+  if (!out || !in || (((uintptr_t)out | (uintptr_t)in) & 15u)) return NTT_EINVAL;
+  if (ranges_overlap(out, batch * p->to * n * 8, in, batch * p->from * n * 8)) return NTT_EOVERLAP;
+  DeviceGuard g(plan->device);
+  if (!g.ok) return NTT_EDEVICE;
+  hipStream_t s = (hipStream_t)stream;
+  const uint32_t tiles = (n + kKsThreads - 1) / kKsThreads;
+  const uint32_t others = p->to - p->from;
+  for (uint64_t b0 = 0; b0 < batch; b0 += kMaxGridY) {
+    const uint64_t nb = std::min(kMaxGridY, batch - b0);
+    // enough blocks to fill the chip; the Garner digits are recomputed per group
+    const uint64_t base = (uint64_t)tiles * nb;
+    const uint32_t groups = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(others, (2048 + base - 1) / base));
+    const dim3 grid(tiles, (uint32_t)nb, groups);
+    uint64_t* o = out + b0 * p->to * n;
+    const uint64_t* x = in + b0 * p->from * n;
+    if (p->below60) {
+      if (p->from <= 4)
+        hipLaunchKernelGGL((modraise_kernel<true, 4>), grid, dim3(kKsThreads), 0, s, o, x, p->moduli, p->garner,
+                           p->eval, plan->logn, p->from, p->to);
+      else
+        hipLaunchKernelGGL((modraise_kernel<true, 16>), grid, dim3(kKsThreads), 0, s, o, x, p->moduli, p->garner,
+                           p->eval, plan->logn, p->from, p->to);
+    } else {
+      if (p->from <= 4)
+        hipLaunchKernelGGL((modraise_kernel<false, 4>), grid, dim3(kKsThreads), 0, s, o, x, p->moduli, p->garner,
+                           p->eval, plan->logn, p->from, p->to);
+      else
+        hipLaunchKernelGGL((modraise_kernel<false, 16>), grid, dim3(kKsThreads), 0, s, o, x, p->moduli, p->garner,
+                           p->eval, plan->logn, p->from, p->to);
+    }
+    if (hipGetLastError() != hipSuccess) return NTT_EDEVICE;
+  }
+  return NTT_OK;
+}
+
+extern "C" void modraise_plan_destroy(ntt_mr_plan* p) {
+  if (!p) return;
+  if (p->d_const) {
+    DeviceGuard g(p->plan->device);
     (void)hipFree(p->d_const);
   }
   delete p;

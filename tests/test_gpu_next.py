@@ -272,3 +272,54 @@ def test_hoisted_validation(B):
     assert call([5, 25], nbytes=nb - 1) == B.NTT_EINVAL
     assert call([5, 25], w=ct) == B.NTT_EOVERLAP
     torch.cuda.synchronize()
+
+
+# ---- modraise ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("logn,bits,frm,to,batch", [(1, 60, 1, 3, 2), (10, 60, 1, 24, 2), (12, 62, 3, 12, 3),
+                                                    (16, 60, 1, 24, 2), (16, 60, 2, 24, 2), (11, 30, 4, 9, 1),
+                                                    (13, 60, 16, 20, 1), (9, 62, 5, 6, 2)])
+def test_modraise_vs_oracle(B, logn, bits, frm, to, batch):
+    n = 1 << logn
+    ps = list(primes(bits, 2 * n, to))
+    plan = B.Plan(n, ps, 0)
+    mr = B.ModRaisePlan(plan, frm, to)
+    x = residues((batch, frm, n), ps[:frm], 8100 + logn + frm)
+    announce("modraise", logn, bits, frm, to, batch)
+    out = dev(np.zeros((batch, to, n), np.uint64))
+    assert_bits_equal(host(B.modraise(mr, out, dev(x))), orc.modraise(x, ps, frm), "modraise")
+
+
+def test_modraise_extremes(B):
+    """Columns at 0 and at Q_from - 1 (all residues q_i - 1)."""
+    n = 1 << 10
+    ps = list(primes(60, 2 * n, 8))
+    plan = B.Plan(n, ps, 0)
+    mr = B.ModRaisePlan(plan, 3, 8)
+    x = residues((1, 3, n), ps[:3], 8200)
+    x[0, :, :100] = 0
+    for i in range(3):
+        x[0, i, 100:200] = ps[i] - 1
+    announce("modraise extremes")
+    out = dev(np.zeros((1, 8, n), np.uint64))
+    assert_bits_equal(host(B.modraise(mr, out, dev(x))), orc.modraise(x, ps, 3), "modraise extremes")
+
+
+def test_modraise_validation(B):
+    import ctypes
+    import torch
+    n = 1 << 10
+    ps = list(primes(60, 2 * n, 8))
+    plan = B.Plan(n, ps, 0)
+    L = B.lib()
+    h = ctypes.c_void_p()
+    assert L.modraise_plan_create(ctypes.byref(h), plan.handle, 0, 4) == B.NTT_EINVAL
+    assert L.modraise_plan_create(ctypes.byref(h), plan.handle, 4, 4) == B.NTT_EINVAL
+    assert L.modraise_plan_create(ctypes.byref(h), plan.handle, 2, 9) == B.NTT_EINVAL
+    mr = B.ModRaisePlan(plan, 2, 8)
+    x = torch.zeros((2, 2, n), dtype=torch.int64, device="cuda:0")
+    out = torch.zeros((2, 8, n), dtype=torch.int64, device="cuda:0")
+    V = ctypes.c_void_p
+    assert L.modraise(mr.handle, V(out.data_ptr()), V(out.data_ptr()), 2, None) == B.NTT_EOVERLAP
+    assert L.modraise(mr.handle, V(out.data_ptr() + 8), V(x.data_ptr()), 2, None) == B.NTT_EINVAL
+    assert L.modraise(mr.handle, V(out.data_ptr()), V(x.data_ptr()), 0, None) == B.NTT_OK
