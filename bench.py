@@ -72,6 +72,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--rotate", type=int, default=3, help="distinct input sets cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-next-rows", action="store_true", help="skip relin / rescale / hoisted / modraise timings")
+    ap.add_argument("--next-reps", type=int, default=10)
     ap.add_argument("--cpu-sample-limbs", type=int, default=384,
                     help="limbs of the batch the oracle processes for the CPU baseline (384 = all 16 polys)")
     return ap.parse_args()
@@ -106,6 +108,73 @@ def cpu_baseline(primes, n, nq, npr, dnum, sample_limbs, a_host, b_host, ct_host
         "sample": (f"{rows} of the 16 polynomials (forward NTT, pointwise, tensor, inverse NTT, automorphism) "
                    f"plus one key-switch: {limb_ntts} limb transforms in {dt:.2f} s"),
     }
+
+
+def time_op(fn, reps):
+    """Mean milliseconds of fn over `reps` calls, HIP events on the current stream."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def next_rows(B, plan, ksp, ws, primes, W, KS, C, ct, ksk, galois, reps):
+    """Timings of the operations that complete a ciphertext product and of the
+    bootstrapping-side ones, on the same workloads (not part of `value`)."""
+    import torch
+    n, L, nq, npr, dnum = W.n, W.limbs, KS.limbs, KS.special, KS.dnum
+    nqp = nq + npr
+    out = {}
+    polys = C.numel() // (L * n)
+    r_out = torch.empty(C.shape[:-2] + (L - 1, n), dtype=torch.int64, device=C.device)
+    for mode, name in ((0, "rescale_truncating"), (1, "rescale_nearest")):
+        ms = time_op(lambda: B.rescale(plan, r_out, C, mode), reps)
+        byts = polys * (2 * L - 1) * n * 8
+        out[name] = {"us": round(ms * 1e3, 2), "alg_GBps": round(byts / (ms * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "shape": f"{polys} polys x {L} -> {L - 1} limbs"}
+    del r_out
+    if ksp is not None:
+        d = torch.empty((1, 3, nq, n), dtype=torch.int64, device=C.device)
+        d[:, :2].copy_(ct)
+        d[:, 2].copy_(ct[:, 1])
+        rel = torch.empty_like(ct)
+        ms_rel = time_op(lambda: B.relinearize(ksp, rel, d, ksk, ws), reps)
+        ms_ks = time_op(lambda: B.keyswitch(ksp, rel, ct, ksk, galois[0], ws), reps)
+        out["relinearize"] = {"us": round(ms_rel * 1e3, 2), "per_s": round(1e3 / ms_rel, 1),
+                              "keyswitch_us_same_run": round(ms_ks * 1e3, 2)}
+        del d, rel
+        R = 8
+        gs = [galois[i % len(galois)] for i in range(R)]
+        keys = ksk.unsqueeze(0).expand(R, *ksk.shape).contiguous()
+        hout = torch.empty((R,) + tuple(ct.shape), dtype=torch.int64, device=C.device)
+        hws = B.hoisted_workspace(ksp, R, 1)
+        ms_h = time_op(lambda: B.keyswitch_hoisted(ksp, hout, ct, keys, gs, hws), reps)
+
+        def separate():
+            for r in range(R):
+                B.keyswitch(ksp, hout[r], ct, keys[r], gs[r], ws)
+        ms_sep = time_op(separate, reps)
+        out["hoisted_rotations"] = {"rotations": R, "us": round(ms_h * 1e3, 2),
+                                    "us_per_rotation": round(ms_h * 1e3 / R, 2),
+                                    "separate_keyswitches_us": round(ms_sep * 1e3, 2),
+                                    "speedup": round(ms_sep / ms_h, 3)}
+        del keys, hout, hws
+    for frm in (1, 2):
+        mr = B.ModRaisePlan(plan, frm, L)
+        x = torch.remainder(C[:2, 0, :frm], 1 << 20).contiguous()  # one ciphertext, residues below every prime
+        y = torch.empty((2, L, n), dtype=torch.int64, device=C.device)
+        ms = time_op(lambda: B.modraise(mr, y, x), reps)
+        byts = 2 * (frm + L) * n * 8
+        out[f"modraise_{frm}_to_{L}"] = {"us": round(ms * 1e3, 2), "alg_GBps": round(byts / (ms * 1e-3) / 1e9, 1)}
+        del x, y, mr
+    return out
 
 
 def main():
@@ -264,6 +333,8 @@ def main():
         "roofline": roofline,
         "input_gen_s": round(gen_s, 2),
     }
+    if not args.no_next_rows:
+        out["next_rows"] = next_rows(B, plan, ksp, ws, primes, W, KS, C, ct, ksk0, galois, args.next_reps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(primes, n, nq, npr, dnum, args.cpu_sample_limbs, a_host, b_host,
                                            ct_host, ksk_host, galois[0])

@@ -18,6 +18,7 @@ struct ModInfo {
   uint64_t n_inv_shoup60;       // floor(n^-1 * 2^62 / q) (primes below 2^60)
   uint32_t n_inv32, n_inv_shoup32;  // narrow (q < 2^30) Shoup pair, else 0
   Barrett br;
+  uint64_t mont_ninv;  // -q^-1 mod 2^64 (Montgomery reduction with R = 2^64)
 };
 
 // Constants to divide by prime k and express the quotient modulo prime l < k (rescale).

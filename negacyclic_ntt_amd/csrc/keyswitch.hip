@@ -117,6 +117,7 @@ struct KsDev {
   const Tw* p_garner;       // [KP][KP]       (KP = kMaxSpecial)
   const Tw* p_eval;         // [nq][KP]
   const Tw* p_inv;          // [nq]
+  const Tw* r_scale;        // [nq+np]  2^64 mod q_t
 };
 
 // ---- ModUp with the automorphism fused on load ---------------------------------
@@ -124,7 +125,9 @@ struct KsDev {
 // Each thread lifts one coefficient of one digit (Garner) and reduces it onto its
 // group's share of the nq + np - alpha other primes: the groups multiply the
 // number of resident waves (the Garner digits are recomputed per group).
-// ext: [batch][dnum][nq+np][n].
+// ext: [batch][dnum][nq+np][n], in Montgomery form: D_j 2^64 mod q_t (the evaluation
+// constants carry the factor 2^64; the digit's own residues are scaled by one Shoup
+// product), so that the key product needs a single Montgomery reduction per output.
 // src: the polynomial that is decomposed, [batch][nq][n] with batch stride src_stride
 // (c1 of a ciphertext, or d2 of a tensor product).
 template <bool B60, int K>
@@ -153,7 +156,8 @@ __global__ __launch_bounds__(kKsThreads) void modup_kernel(uint64_t* __restrict_
 #pragma unroll
     for (int i = 0; i < K; ++i) {
       if (i >= (int)alpha) break;
-      out[(uint64_t)(first + i) * n] = x[i];  // the digit's own primes keep their residues
+      const uint64_t q = kc.moduli[first + i];  // the digit's own primes keep their residues
+      out[(uint64_t)(first + i) * n] = csub(shoup<B60>(x[i], kc.r_scale[first + i], q), q);
     }
   }
   constexpr int S = kMaxDigitPrimes;
@@ -170,33 +174,53 @@ __global__ __launch_bounds__(kKsThreads) void modup_kernel(uint64_t* __restrict_
 }
 
 // ---- key inner product -----------------------------------------------------------
-// acc[b][c][t][e] = sum_j ext[b][j][t][e] * ksk[j][c][t][e]  (mod q_t), two coefficients per thread.
+// acc[b][c][t][e] = sum_j ext[b][j][t][e] * ksk[j][c][t][e]  (mod q_t), two coefficients
+// per thread.  The digits carry a factor 2^64, so the exact 128-bit sum of up to
+// `chunk` products (chunk q_t <= 2^64 keeps it below q_t 2^64) is Montgomery-reduced
+// once to the plain residue.
+struct MacSum {
+  Acc128 t{0, 0};
+  uint64_t r = 0;  // reduced chunks, canonical
+  __device__ __forceinline__ void fold(uint64_t q, uint64_t ninv) {
+    r = add_mod(r, csub(redc(t, q, ninv), q), q);
+    t = Acc128{0, 0};
+  }
+};
+
 __global__ __launch_bounds__(kKsThreads) void mac_kernel(uint64_t* __restrict__ acc, const uint64_t* __restrict__ ext,
                                                          const uint64_t* __restrict__ ksk,
                                                          const ModInfo* __restrict__ mods, uint32_t logn,
-                                                         uint32_t nqp, uint32_t dnum, uint64_t pairs_per_batch) {
+                                                         uint32_t nqp, uint32_t dnum, uint32_t chunk,
+                                                         uint64_t pairs_per_batch) {
   const uint64_t p = (uint64_t)blockIdx.x * kKsThreads + threadIdx.x;
   const uint32_t b = blockIdx.y;
   if (p >= pairs_per_batch) return;
   const uint64_t off = 2 * p;  // index in [nqp][n]
   const uint32_t t = (uint32_t)(off >> logn);
-  const Barrett br = mods[t].br;
-  const uint64_t q = br.q;
+  const uint64_t q = mods[t].q, ninv = mods[t].mont_ninv;
   const uint64_t plane = (uint64_t)nqp << logn;
   const uint64_t* xe = ext + (uint64_t)b * dnum * plane + off;
-  ulonglong2 s0 = {0, 0}, s1 = {0, 0};
+  MacSum s0x, s0y, s1x, s1y;
+  uint32_t c = 0;
   for (uint32_t j = 0; j < dnum; ++j) {
     const ulonglong2 d = *reinterpret_cast<const ulonglong2*>(xe + (uint64_t)j * plane);
     const ulonglong2 k0 = *reinterpret_cast<const ulonglong2*>(ksk + ((uint64_t)j * 2) * plane + off);
     const ulonglong2 k1 = *reinterpret_cast<const ulonglong2*>(ksk + ((uint64_t)j * 2 + 1) * plane + off);
-    s0.x = add_mod(s0.x, barrett_mul(d.x, k0.x, br), q);
-    s0.y = add_mod(s0.y, barrett_mul(d.y, k0.y, br), q);
-    s1.x = add_mod(s1.x, barrett_mul(d.x, k1.x, br), q);
-    s1.y = add_mod(s1.y, barrett_mul(d.y, k1.y, br), q);
+    mac128(s0x.t, d.x, k0.x);
+    mac128(s0y.t, d.y, k0.y);
+    mac128(s1x.t, d.x, k1.x);
+    mac128(s1y.t, d.y, k1.y);
+    if (++c == chunk || j + 1 == dnum) {
+      s0x.fold(q, ninv);
+      s0y.fold(q, ninv);
+      s1x.fold(q, ninv);
+      s1y.fold(q, ninv);
+      c = 0;
+    }
   }
   uint64_t* o = acc + (uint64_t)b * 2 * plane + off;
-  *reinterpret_cast<ulonglong2*>(o) = s0;
-  *reinterpret_cast<ulonglong2*>(o + plane) = s1;
+  *reinterpret_cast<ulonglong2*>(o) = ulonglong2{s0x.r, s0y.r};
+  *reinterpret_cast<ulonglong2*>(o + plane) = ulonglong2{s1x.r, s1y.r};
 }
 
 // ---- key inner product for hoisted rotations -------------------------------------------
@@ -228,7 +252,8 @@ __global__ __launch_bounds__(kKsThreads) void mac_hoisted_kernel(uint64_t* __res
                                                                  const uint64_t* __restrict__ ksk,
                                                                  const ModInfo* __restrict__ mods, uint32_t logn,
                                                                  uint32_t seglog, uint32_t nqp, uint32_t dnum,
-                                                                 uint32_t R, uint32_t batch, HoistArgs ha) {
+                                                                 uint32_t chunk, uint32_t R, uint32_t batch,
+                                                                 HoistArgs ha) {
   extern __shared__ uint64_t seg_lds[];  // [dnum][seg]
   const uint32_t seg = 1u << seglog, nseg = 1u << (logn - seglog);
   const uint32_t t = blockIdx.x >> (logn - seglog), s0 = (blockIdx.x & (nseg - 1)) << seglog;
@@ -247,26 +272,33 @@ __global__ __launch_bounds__(kKsThreads) void mac_hoisted_kernel(uint64_t* __res
   }
   __syncthreads();
   if (!active) return;
-  const Barrett br = mods[t].br;
-  const uint64_t q = br.q;
+  const uint64_t q = mods[t].q, ninv = mods[t].mont_ninv;
   for (uint32_t r = 0; r < R; ++r) {
     const uint32_t g = ha.g[r];
     const uint32_t k0 = (ntt_slot(s0, ha.h[r], logn) & ~(seg - 1)) + i2;
     const uint32_t p0 = ntt_slot(k0, g, logn) - s0, p1 = ntt_slot(k0 + 1, g, logn) - s0;
     const uint64_t* kr = ksk + (uint64_t)r * dnum * 2 * plane + row + k0;
-    ulonglong2 a0 = {0, 0}, a1 = {0, 0};
+    MacSum s0x, s0y, s1x, s1y;
+    uint32_t c = 0;
     for (uint32_t j = 0; j < dnum; ++j) {
       const uint64_t d0 = seg_lds[j * seg + p0], d1 = seg_lds[j * seg + p1];
       const ulonglong2 k0v = *reinterpret_cast<const ulonglong2*>(kr + (uint64_t)(2 * j) * plane);
       const ulonglong2 k1v = *reinterpret_cast<const ulonglong2*>(kr + (uint64_t)(2 * j + 1) * plane);
-      a0.x = add_mod(a0.x, barrett_mul(d0, k0v.x, br), q);
-      a0.y = add_mod(a0.y, barrett_mul(d1, k0v.y, br), q);
-      a1.x = add_mod(a1.x, barrett_mul(d0, k1v.x, br), q);
-      a1.y = add_mod(a1.y, barrett_mul(d1, k1v.y, br), q);
+      mac128(s0x.t, d0, k0v.x);
+      mac128(s0y.t, d1, k0v.y);
+      mac128(s1x.t, d0, k1v.x);
+      mac128(s1y.t, d1, k1v.y);
+      if (++c == chunk || j + 1 == dnum) {
+        s0x.fold(q, ninv);
+        s0y.fold(q, ninv);
+        s1x.fold(q, ninv);
+        s1y.fold(q, ninv);
+        c = 0;
+      }
     }
     uint64_t* o = acc + ((uint64_t)r * batch + b) * 2 * plane + row + k0;
-    *reinterpret_cast<ulonglong2*>(o) = a0;
-    *reinterpret_cast<ulonglong2*>(o + plane) = a1;
+    *reinterpret_cast<ulonglong2*>(o) = ulonglong2{s0x.r, s0y.r};
+    *reinterpret_cast<ulonglong2*>(o + plane) = ulonglong2{s1x.r, s1y.r};
   }
 }
 
@@ -276,15 +308,23 @@ __global__ __launch_bounds__(kKsThreads) void mac_hoisted_kernel(uint64_t* __res
 // acc: [batch][2][nq+np][n].  Output component c gets sigma_g(add[b][c]) added when
 // bit c of add_mask is set (add: [batch][*][nq][n], batch stride add_stride): c0 for
 // a rotation, (d0, d1) for a relinearisation.
+// grid.z = rotations x groups: rotation r (hoisted rotations; 0 otherwise) reads
+// acc + r acc_rot, writes out + r out_rot and gathers the additive input through
+// sigma with h = ha.h[r].
 template <bool B60, int KP>
 __global__ __launch_bounds__(kKsThreads) void moddown_kernel(uint64_t* __restrict__ out,
                                                              const uint64_t* __restrict__ acc,
                                                              const uint64_t* __restrict__ add, uint64_t add_stride,
-                                                             uint32_t add_mask, KsDev kc, uint32_t logn, uint32_t h,
-                                                             uint32_t nq, uint32_t np_) {
+                                                             uint32_t add_mask, KsDev kc, uint32_t logn, uint32_t nq,
+                                                             uint32_t np_, uint32_t groups, uint64_t out_rot,
+                                                             uint64_t acc_rot, HoistArgs ha) {
   const uint32_t n = 1u << logn;
   const uint32_t e = blockIdx.x * kKsThreads + threadIdx.x;
   if (e >= n) return;
+  const uint32_t rot = blockIdx.z / groups, grp = blockIdx.z % groups;
+  const uint32_t h = ha.h[rot];
+  out += rot * out_rot;
+  acc += rot * acc_rot;
   const uint32_t bc = blockIdx.y, b = bc >> 1, comp = bc & 1;
   const uint32_t nqp = nq + np_;
   const uint64_t* a = acc + (uint64_t)bc * nqp * n + e;
@@ -300,8 +340,8 @@ __global__ __launch_bounds__(kKsThreads) void moddown_kernel(uint64_t* __restric
   const uint64_t* c0 = add + (uint64_t)b * add_stride + (uint64_t)comp * nq * n;
   const Gather gi = gather_index(e, h, logn);
   uint64_t* o = out + (uint64_t)bc * nq * n + e;
-  const uint32_t per = (nq + gridDim.z - 1) / gridDim.z;
-  const uint32_t l0 = blockIdx.z * per, l1 = min(nq, l0 + per);
+  const uint32_t per = (nq + groups - 1) / groups;
+  const uint32_t l0 = grp * per, l1 = min(nq, l0 + per);
 #pragma unroll 4
   for (uint32_t l = l0; l < l1; ++l) {
     const uint64_t q = kc.moduli[l];
@@ -364,7 +404,8 @@ using namespace nntt;
 struct ntt_ks_plan {
   const ntt_plan* qp = nullptr;
   uint32_t nq = 0, np = 0, dnum = 0, alpha = 0;
-  bool below60 = false;  // every prime of Q u P below 2^60
+  uint32_t mac_chunk = 1;  // products summed before a Montgomery reduction: chunk q < 2^64
+  bool below60 = false;    // every prime of Q u P below 2^60
   void* d_const = nullptr;
   KsDev dev{};
 };
@@ -387,9 +428,9 @@ void garner_table(const uint64_t* m, uint32_t k, uint32_t K, Tw* g) {
   }
 }
 
-// c[i] = prod_{j<i} m_j mod p
-void eval_table(const uint64_t* m, uint32_t k, uint64_t p, Tw* c) {
-  uint64_t prod = 1 % p;
+// c[i] = scale * prod_{j<i} m_j mod p
+void eval_table(const uint64_t* m, uint32_t k, uint64_t p, Tw* c, uint64_t scale = 1) {
+  uint64_t prod = scale % p;
   for (uint32_t i = 0; i < k; ++i) {
     c[i] = shoup_pair(prod, p);
     prod = host_mulmod(prod, m[i] % p, p);
@@ -412,10 +453,16 @@ extern "C" int keyswitch_plan_create(ntt_ks_plan** out, const ntt_plan* qp, uint
 
   std::vector<uint64_t> moduli(m, m + nqp);
   std::vector<Tw> dg((size_t)dnum * K * K, Tw{0, 0}), de((size_t)dnum * nqp * K, Tw{0, 0});
-  std::vector<Tw> pg((size_t)KP * KP, Tw{0, 0}), pe((size_t)nq * KP, Tw{0, 0}), pinv(nq);
+  std::vector<Tw> pg((size_t)KP * KP, Tw{0, 0}), pe((size_t)nq * KP, Tw{0, 0}), pinv(nq), rs(nqp);
+  uint64_t qmax = 0;
+  for (uint32_t t = 0; t < nqp; ++t) {
+    rs[t] = shoup_pair((uint64_t)(((unsigned __int128)1 << 64) % m[t]), m[t]);  // 2^64 mod q_t
+    qmax = std::max(qmax, m[t]);
+  }
   for (uint32_t j = 0; j < dnum; ++j) {
     garner_table(m + j * alpha, alpha, K, dg.data() + (size_t)j * K * K);
-    for (uint32_t t = 0; t < nqp; ++t) eval_table(m + j * alpha, alpha, m[t], de.data() + ((size_t)j * nqp + t) * K);
+    for (uint32_t t = 0; t < nqp; ++t)  // digits are written in Montgomery form (times 2^64)
+      eval_table(m + j * alpha, alpha, m[t], de.data() + ((size_t)j * nqp + t) * K, rs[t].w);
   }
   garner_table(m + nq, np_, KP, pg.data());
   for (uint32_t l = 0; l < nq; ++l) {
@@ -427,13 +474,14 @@ extern "C" int keyswitch_plan_create(ntt_ks_plan** out, const ntt_plan* qp, uint
 
   const size_t sz_m = moduli.size() * 8, sz_dg = dg.size() * sizeof(Tw), sz_de = de.size() * sizeof(Tw);
   const size_t sz_pg = pg.size() * sizeof(Tw), sz_pe = pe.size() * sizeof(Tw), sz_pi = pinv.size() * sizeof(Tw);
+  const size_t sz_rs = rs.size() * sizeof(Tw);
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  const size_t total = al(sz_m) + al(sz_dg) + al(sz_de) + al(sz_pg) + al(sz_pe) + al(sz_pi);
+  const size_t total = al(sz_m) + al(sz_dg) + al(sz_de) + al(sz_pg) + al(sz_pe) + al(sz_pi) + al(sz_rs);
   std::vector<uint8_t> blob(total, 0);
-  size_t off[6], o = 0;
-  const void* src[6] = {moduli.data(), dg.data(), de.data(), pg.data(), pe.data(), pinv.data()};
-  const size_t sz[6] = {sz_m, sz_dg, sz_de, sz_pg, sz_pe, sz_pi};
-  for (int i = 0; i < 6; ++i) {
+  size_t off[7], o = 0;
+  const void* src[7] = {moduli.data(), dg.data(), de.data(), pg.data(), pe.data(), pinv.data(), rs.data()};
+  const size_t sz[7] = {sz_m, sz_dg, sz_de, sz_pg, sz_pe, sz_pi, sz_rs};
+  for (int i = 0; i < 7; ++i) {
     off[i] = o;
     memcpy(blob.data() + o, src[i], sz[i]);
     o += al(sz[i]);
@@ -470,6 +518,8 @@ extern "C" int keyswitch_plan_create(ntt_ks_plan** out, const ntt_plan* qp, uint
   p->dev.p_garner = (const Tw*)(base + off[3]);
   p->dev.p_eval = (const Tw*)(base + off[4]);
   p->dev.p_inv = (const Tw*)(base + off[5]);
+  p->dev.r_scale = (const Tw*)(base + off[6]);
+  p->mac_chunk = (uint32_t)std::min<uint64_t>(dnum, ~0ull / qmax);
   *out = p;
   return NTT_OK;
 }
@@ -530,9 +580,9 @@ void launch_modup(dim3 grid, hipStream_t s, uint64_t* ext, const KsIo& io, const
 
 template <bool B60, int KP>
 void launch_moddown(dim3 grid, hipStream_t s, uint64_t* out, const uint64_t* acc, const KsIo& io,
-                    const ntt_ks_plan* p, uint32_t h) {
+                    const ntt_ks_plan* p, uint32_t groups, uint64_t out_rot, uint64_t acc_rot, const HoistArgs& ha) {
   hipLaunchKernelGGL((moddown_kernel<B60, KP>), grid, dim3(kKsThreads), 0, s, out, acc, io.add, io.add_stride,
-                     io.add_mask, p->dev, p->qp->logn, h, p->nq, p->np);
+                     io.add_mask, p->dev, p->qp->logn, p->nq, p->np, groups, out_rot, acc_rot, ha);
 }
 
 constexpr uint64_t kMaxGridY = 65535;
@@ -565,27 +615,30 @@ int ks_modup(const ntt_ks_plan* p, uint64_t* ext, const KsIo& io, uint32_t h, ui
   return NTT_OK;
 }
 
-// ModDown of acc [batch][2][nqp][n] into out [batch][2][nq][n], adding the sigma_h
-// gathered additive inputs selected by io.add_mask.
-int ks_moddown(const ntt_ks_plan* p, uint64_t* out, const uint64_t* acc, const KsIo& io, uint32_t h, uint64_t batch,
-               hipStream_t s) {
+// ModDown of acc [R][batch][2][nqp][n] into out [R][batch][2][nq][n], adding the
+// sigma_{h_r} gathered additive inputs selected by io.add_mask (R = num_rot, with
+// ha.h[r] the inverse Galois element of rotation r).  One launch covers every
+// rotation (grid.z = R x groups).
+int ks_moddown(const ntt_ks_plan* p, uint64_t* out, const uint64_t* acc, const KsIo& io, const HoistArgs& ha,
+               uint32_t num_rot, uint64_t batch, hipStream_t s) {
   const uint32_t n = p->qp->n, nq = p->nq, nqp = nq + p->np;
   const uint32_t tiles = (n + kKsThreads - 1) / kKsThreads;
-  const uint32_t down_groups = std::max(1u, std::min(kModDownGroups, nq));
+  const uint32_t groups = std::max(1u, std::min(kModDownGroups, nq));
+  const uint64_t out_rot = batch * 2 * nq * n, acc_rot = batch * 2 * nqp * n;
   const uint64_t down_chunk = kMaxGridY / 2;
   for (uint64_t b0 = 0; b0 < batch; b0 += down_chunk) {
     const uint64_t nb = std::min(down_chunk, batch - b0);
     KsIo c = io;
     c.add += b0 * io.add_stride;
-    const dim3 grid(tiles, (uint32_t)(nb * 2), down_groups);
+    const dim3 grid(tiles, (uint32_t)(nb * 2), num_rot * groups);
     uint64_t* o = out + b0 * 2 * nq * n;
     const uint64_t* a = acc + b0 * 2 * nqp * n;
     if (p->below60) {
-      if (p->np <= 8) launch_moddown<true, 8>(grid, s, o, a, c, p, h);
-      else launch_moddown<true, 16>(grid, s, o, a, c, p, h);
+      if (p->np <= 8) launch_moddown<true, 8>(grid, s, o, a, c, p, groups, out_rot, acc_rot, ha);
+      else launch_moddown<true, 16>(grid, s, o, a, c, p, groups, out_rot, acc_rot, ha);
     } else {
-      if (p->np <= 8) launch_moddown<false, 8>(grid, s, o, a, c, p, h);
-      else launch_moddown<false, 16>(grid, s, o, a, c, p, h);
+      if (p->np <= 8) launch_moddown<false, 8>(grid, s, o, a, c, p, groups, out_rot, acc_rot, ha);
+      else launch_moddown<false, 16>(grid, s, o, a, c, p, groups, out_rot, acc_rot, ha);
     }
     if (hipGetLastError() != hipSuccess) return NTT_EDEVICE;
   }
@@ -615,11 +668,13 @@ int ks_run(const ntt_ks_plan* p, uint64_t* out, const KsIo& io, const uint64_t* 
     const uint64_t nb = std::min(kMaxGridY, batch - b0);
     hipLaunchKernelGGL(mac_kernel, dim3((uint32_t)((pairs + kKsThreads - 1) / kKsThreads), (uint32_t)nb),
                        dim3(kKsThreads), 0, s, acc + b0 * 2 * nqp * n, ext + b0 * dnum * nqp * n, ksk, qp->d_mods,
-                       qp->logn, nqp, dnum, pairs);
+                       qp->logn, nqp, dnum, p->mac_chunk, pairs);
     if (hipGetLastError() != hipSuccess) return NTT_EDEVICE;
   }
   if (launch_ntt(qp, acc, batch * 2, 0, nqp, true, s) != hipSuccess) return NTT_EDEVICE;
-  return ks_moddown(p, out, acc, io, h, batch, s);
+  HoistArgs ha{};
+  ha.h[0] = h;
+  return ks_moddown(p, out, acc, io, ha, 1, batch, s);
 }
 }  // namespace
 
@@ -698,15 +753,10 @@ extern "C" int keyswitch_hoisted(const ntt_ks_plan* p, uint64_t* out, const uint
   const uint32_t seglog = std::min(qp->logn, 9u);
   const dim3 grid((nqp << (qp->logn - seglog)), (uint32_t)batch);
   hipLaunchKernelGGL(mac_hoisted_kernel, grid, dim3(kKsThreads), (size_t)dnum * (8u << seglog), s, acc, ext, ksk,
-                     qp->d_mods, qp->logn, seglog, nqp, dnum, num_rot, (uint32_t)batch, ha);
+                     qp->d_mods, qp->logn, seglog, nqp, dnum, p->mac_chunk, num_rot, (uint32_t)batch, ha);
   if (hipGetLastError() != hipSuccess) return NTT_EDEVICE;
   if (launch_ntt(qp, acc, batch * 2 * num_rot, 0, nqp, true, s) != hipSuccess) return NTT_EDEVICE;
-  for (uint32_t r = 0; r < num_rot; ++r) {
-    rc = ks_moddown(p, out + (uint64_t)r * batch * 2 * plane, acc + (uint64_t)r * batch * 2 * qplane, io, ha.h[r],
-                    batch, s);
-    if (rc) return rc;
-  }
-  return NTT_OK;
+  return ks_moddown(p, out, acc, io, ha, num_rot, batch, s);
 }
 
 extern "C" void keyswitch_plan_destroy(ntt_ks_plan* p) {

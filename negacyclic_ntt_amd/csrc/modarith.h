@@ -173,6 +173,24 @@ __device__ __forceinline__ uint64_t barrett_mul(uint64_t a, uint64_t c, const Ba
   return barrett_reduce(__umul64hi(a, c), a * c, b);
 }
 
+// Exact 128-bit accumulation of 64 x 64-bit products, and Montgomery reduction with
+// R = 2^64: for T = hi 2^64 + lo < q 2^64 and ninv = -q^-1 mod 2^64, m = lo ninv
+// makes T + m q divisible by 2^64; the quotient hi + hi64(m q) + [lo != 0] equals
+// T 2^-64 mod q and lies in [0, 2q).  (lo + lo64(m q) is 0 or exactly 2^64.)
+struct Acc128 {
+  uint64_t lo, hi;
+};
+__device__ __forceinline__ void mac128(Acc128& a, uint64_t x, uint64_t y) {
+  const uint64_t lo = x * y;
+  a.hi += __umul64hi(x, y);
+  a.lo += lo;
+  a.hi += (a.lo < lo);
+}
+__device__ __forceinline__ uint64_t redc(const Acc128& a, uint64_t q, uint64_t ninv) {
+  const uint64_t m = a.lo * ninv;
+  return a.hi + __umul64hi(m, q) + (a.lo != 0);
+}
+
 __device__ __forceinline__ uint64_t add_mod(uint64_t a, uint64_t c, uint64_t q) { return csub(a + c, q); }
 __device__ __forceinline__ uint64_t sub_mod(uint64_t a, uint64_t c, uint64_t q) { return a >= c ? a - c : a + q - c; }
 __device__ __forceinline__ uint64_t neg_mod(uint64_t a, uint64_t q) { return a ? q - a : 0; }

@@ -284,6 +284,9 @@ extern "C" int ntt_plan_create(ntt_plan** out, uint32_t n, const uint64_t* prime
       m.n_inv_shoup32 = (uint32_t)(((uint64_t)m.n_inv << 32) / q);
     }
     m.br = host_barrett(q);
+    uint64_t inv = q;  // Newton: q * q == 1 mod 8, each step doubles the correct bits
+    for (int it = 0; it < 5; ++it) inv *= 2 - q * inv;
+    m.mont_ninv = 0 - inv;
   }
 
   if (device >= 0) {
