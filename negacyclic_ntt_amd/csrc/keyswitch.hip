@@ -97,6 +97,54 @@ __device__ __forceinline__ uint64_t mixed_radix_eval(const uint64_t (&v)[K], uin
   return csub(s, p);
 }
 
+// Below 2^60: sum_i v_i c_i for digits v_i < 2^60 and constants c_i < p stored as
+// 30-bit halves.  Each term is four carry-free 32 x 32 + 64-bit multiply-adds into
+//   A = sum vl cl,  B = sum (vl ch + vh cl),  C = sum vh ch
+// (per term below 2^60, 2^61, 2^60, so eight terms cannot overflow); the exact
+// T = A + B 2^30 + C 2^60 < 8 2^60 p < p 2^64 is then Montgomery-reduced once.  The
+// constants carry the factor 2^64 that the reduction divides out.  Result canonical.
+struct C30 {
+  uint32_t l, h;
+};
+template <int K>
+__device__ __forceinline__ uint64_t dot30(const uint32_t (&vl)[K], const uint32_t (&vh)[K], uint32_t k,
+                                          const C30* __restrict__ c, uint64_t p, uint64_t ninv) {
+  uint64_t r = 0;
+#pragma unroll
+  for (int i0 = 0; i0 < K; i0 += 8) {
+    if (i0 >= (int)k) break;
+    uint64_t A = 0, B = 0, C = 0;
+#pragma unroll
+    for (int i = i0; i < i0 + 8 && i < K; ++i) {
+      if (i >= (int)k) break;
+      const C30 cc = c[i];
+      A += (uint64_t)vl[i] * cc.l;
+      B += (uint64_t)vl[i] * cc.h;
+      B += (uint64_t)vh[i] * cc.l;
+      C += (uint64_t)vh[i] * cc.h;
+    }
+    const uint64_t blo = B << 30, clo = C << 60;
+    Acc128 t;
+    t.lo = A + blo;
+    t.hi = (B >> 34) + (C >> 4) + (t.lo < blo);
+    t.lo += clo;
+    t.hi += (t.lo < clo);
+    const uint64_t red = csub(redc(t, p, ninv), p);
+    r = i0 == 0 ? red : add_mod(r, red, p);
+  }
+  return r;
+}
+
+template <int K>
+__device__ __forceinline__ void split30(const uint64_t (&v)[K], uint32_t (&vl)[K], uint32_t (&vh)[K], uint32_t k) {
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    if (i >= (int)k) break;
+    vl[i] = (uint32_t)v[i] & 0x3fffffffu;
+    vh[i] = (uint32_t)(v[i] >> 30);
+  }
+}
+
 // Coefficient-domain automorphism gather: value of sigma_g(a) at position e.
 // i = e * h mod 2n with h = g^-1 mod 2n; sigma_g(a)[e] = a[i] (i < n) or -a[i - n].
 struct Gather {
@@ -118,6 +166,9 @@ struct KsDev {
   const Tw* p_eval;         // [nq][KP]
   const Tw* p_inv;          // [nq]
   const Tw* r_scale;        // [nq+np]  2^64 mod q_t
+  const C30* digit_eval30;  // [dnum][nq+np][K]  below 2^60: digit products times 2^128 mod q_t
+  const C30* p_eval30;      // [nq][KP]           below 2^60: products of P's primes times 2^64
+  const uint64_t* ninv;     // [nq+np]  -q_t^-1 mod 2^64
 };
 
 // ---- ModUp with the automorphism fused on load ---------------------------------
@@ -166,10 +217,21 @@ __global__ __launch_bounds__(kKsThreads) void modup_kernel(uint64_t* __restrict_
   // targets m = 0 .. nqp - alpha - 1 skip the digit's own primes: t = m or m + alpha
   const uint32_t others = nqp - alpha, per = (others + gridDim.z - 1) / gridDim.z;
   const uint32_t m0 = blockIdx.z * per, m1 = min(others, m0 + per);
+  if constexpr (B60) {
+    uint32_t vl[K], vh[K];
+    split30<K>(v, vl, vh, alpha);
+    const C30* ev30 = kc.digit_eval30 + (size_t)j * nqp * S;
+#pragma unroll 2
+    for (uint32_t m = m0; m < m1; ++m) {
+      const uint32_t t = m < first ? m : m + alpha;
+      out[(uint64_t)t * n] = dot30<K>(vl, vh, alpha, ev30 + (size_t)t * S, kc.moduli[t], kc.ninv[t]);
+    }
+  } else {
 #pragma unroll 4
-  for (uint32_t m = m0; m < m1; ++m) {
-    const uint32_t t = m < first ? m : m + alpha;
-    out[(uint64_t)t * n] = mixed_radix_eval<B60, K>(v, alpha, ev + (size_t)t * S, kc.moduli[t]);
+    for (uint32_t m = m0; m < m1; ++m) {
+      const uint32_t t = m < first ? m : m + alpha;
+      out[(uint64_t)t * n] = mixed_radix_eval<B60, K>(v, alpha, ev + (size_t)t * S, kc.moduli[t]);
+    }
   }
 }
 
@@ -342,10 +404,14 @@ __global__ __launch_bounds__(kKsThreads) void moddown_kernel(uint64_t* __restric
   uint64_t* o = out + (uint64_t)bc * nq * n + e;
   const uint32_t per = (nq + groups - 1) / groups;
   const uint32_t l0 = grp * per, l1 = min(nq, l0 + per);
+  uint32_t vl[KP], vh[KP];
+  if constexpr (B60) split30<KP>(v, vl, vh, np_);
 #pragma unroll 4
   for (uint32_t l = l0; l < l1; ++l) {
     const uint64_t q = kc.moduli[l];
-    const uint64_t r = mixed_radix_eval<B60, KP>(v, np_, kc.p_eval + (size_t)l * S, q);  // (X mod P) mod q_l
+    uint64_t r;  // (X mod P) mod q_l
+    if constexpr (B60) r = dot30<KP>(vl, vh, np_, kc.p_eval30 + (size_t)l * S, q, kc.ninv[l]);
+    else r = mixed_radix_eval<B60, KP>(v, np_, kc.p_eval + (size_t)l * S, q);
     const uint64_t d = sub_mod(a[(uint64_t)l * n], r, q);
     uint64_t res = csub(shoup<B60>(d, kc.p_inv[l], q), q);
     if (adds) {
@@ -464,9 +530,24 @@ extern "C" int keyswitch_plan_create(ntt_ks_plan** out, const ntt_plan* qp, uint
     for (uint32_t t = 0; t < nqp; ++t)  // digits are written in Montgomery form (times 2^64)
       eval_table(m + j * alpha, alpha, m[t], de.data() + ((size_t)j * nqp + t) * K, rs[t].w);
   }
+  // Below 2^60 the evaluations use 30-bit halves and one Montgomery reduction, which
+  // divides by 2^64: the digit constants carry 2^128 (result times 2^64), P's 2^64.
+  std::vector<C30> de30((size_t)dnum * nqp * K, C30{0, 0}), pe30((size_t)nq * KP, C30{0, 0});
+  std::vector<uint64_t> ninv(nqp);
+  auto split = [](uint64_t c) { return C30{(uint32_t)(c & 0x3fffffffu), (uint32_t)(c >> 30)}; };
+  for (uint32_t t = 0; t < nqp; ++t) ninv[t] = qp->h_mods[t].mont_ninv;
+  if (range_below60(qp, 0, nqp)) {
+    for (size_t i = 0; i < de30.size(); ++i) {
+      const uint32_t t = (uint32_t)((i / K) % nqp);
+      de30[i] = split(host_mulmod(de[i].w, rs[t].w, m[t]));
+    }
+  }
   garner_table(m + nq, np_, KP, pg.data());
   for (uint32_t l = 0; l < nq; ++l) {
     eval_table(m + nq, np_, m[l], pe.data() + (size_t)l * KP);
+    if (range_below60(qp, 0, nqp))
+      for (uint32_t i = 0; i < np_; ++i)
+        pe30[(size_t)l * KP + i] = split(host_mulmod(pe[(size_t)l * KP + i].w, rs[l].w, m[l]));
     uint64_t P = 1;
     for (uint32_t i = 0; i < np_; ++i) P = host_mulmod(P, m[nq + i] % m[l], m[l]);
     pinv[l] = shoup_pair(host_invmod(P, m[l]), m[l]);
@@ -474,14 +555,18 @@ extern "C" int keyswitch_plan_create(ntt_ks_plan** out, const ntt_plan* qp, uint
 
   const size_t sz_m = moduli.size() * 8, sz_dg = dg.size() * sizeof(Tw), sz_de = de.size() * sizeof(Tw);
   const size_t sz_pg = pg.size() * sizeof(Tw), sz_pe = pe.size() * sizeof(Tw), sz_pi = pinv.size() * sizeof(Tw);
-  const size_t sz_rs = rs.size() * sizeof(Tw);
+  const size_t sz_rs = rs.size() * sizeof(Tw), sz_d30 = de30.size() * sizeof(C30), sz_p30 = pe30.size() * sizeof(C30);
+  const size_t sz_ni = ninv.size() * 8;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  const size_t total = al(sz_m) + al(sz_dg) + al(sz_de) + al(sz_pg) + al(sz_pe) + al(sz_pi) + al(sz_rs);
+  constexpr int kParts = 10;
+  const void* src[kParts] = {moduli.data(), dg.data(), de.data(),   pg.data(),   pe.data(),
+                             pinv.data(),   rs.data(), de30.data(), pe30.data(), ninv.data()};
+  const size_t sz[kParts] = {sz_m, sz_dg, sz_de, sz_pg, sz_pe, sz_pi, sz_rs, sz_d30, sz_p30, sz_ni};
+  size_t total = 0;
+  for (int i = 0; i < kParts; ++i) total += al(sz[i]);
   std::vector<uint8_t> blob(total, 0);
-  size_t off[7], o = 0;
-  const void* src[7] = {moduli.data(), dg.data(), de.data(), pg.data(), pe.data(), pinv.data(), rs.data()};
-  const size_t sz[7] = {sz_m, sz_dg, sz_de, sz_pg, sz_pe, sz_pi, sz_rs};
-  for (int i = 0; i < 7; ++i) {
+  size_t off[kParts], o = 0;
+  for (int i = 0; i < kParts; ++i) {
     off[i] = o;
     memcpy(blob.data() + o, src[i], sz[i]);
     o += al(sz[i]);
@@ -519,6 +604,9 @@ extern "C" int keyswitch_plan_create(ntt_ks_plan** out, const ntt_plan* qp, uint
   p->dev.p_eval = (const Tw*)(base + off[4]);
   p->dev.p_inv = (const Tw*)(base + off[5]);
   p->dev.r_scale = (const Tw*)(base + off[6]);
+  p->dev.digit_eval30 = (const C30*)(base + off[7]);
+  p->dev.p_eval30 = (const C30*)(base + off[8]);
+  p->dev.ninv = (const uint64_t*)(base + off[9]);
   p->mac_chunk = (uint32_t)std::min<uint64_t>(dnum, ~0ull / qmax);
   *out = p;
   return NTT_OK;
