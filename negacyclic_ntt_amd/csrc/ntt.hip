@@ -61,14 +61,17 @@ constexpr Sched make_sched(int logm) {
   return S;
 }
 
+#ifndef NNTT_LDS_PAD
+#define NNTT_LDS_PAD 1
+#endif
 template <class A>
 constexpr int sub_stride(int m) {
-  return (1 << m) + ((1 << m) >> A::kPadShift) + 1;
+  return NNTT_LDS_PAD ? (1 << m) + ((1 << m) >> A::kPadShift) + 1 : (1 << m);
 }
 
 template <class A>
 __device__ __forceinline__ int lpos(int pos) {
-  return pos + (pos >> A::kPadShift);
+  return NNTT_LDS_PAD ? pos + (pos >> A::kPadShift) : pos;
 }
 
 // Work placement.  Hardware block b is dispatched to XCD b % 8 of the MI355X.  The
@@ -251,7 +254,10 @@ __global__ __launch_bounds__(LdsCfg<LOGN>::NT) void ntt_lds_kernel(uint64_t* dat
   if (ROWS == 1) row0 = place_block(1, total_rows / num_limbs, num_limbs, 0).row;
 
   // Coalesced load, two residues per thread per step.
-  for (int e = 2 * tid; e < ROWS * N; e += 2 * NT) {
+  static_assert((ROWS * N) % (2 * NT) == 0, "whole iterations");
+#pragma unroll
+  for (int it = 0; it < (ROWS * N) / (2 * NT); ++it) {
+    const int e = 2 * tid + it * 2 * NT;
     const int sub = e / N, pos = e % N;
     if (row0 + sub < total_rows) {
       const ulonglong2 v = *reinterpret_cast<const ulonglong2*>(in + (row0 + sub) * N + pos);
@@ -280,7 +286,10 @@ __global__ __launch_bounds__(LdsCfg<LOGN>::NT) void ntt_lds_kernel(uint64_t* dat
   };
   run_passes<A, FWD, LOGN, ROWS, NT, 0>(lds, tid, get_sub);
 
-  for (int e = 2 * tid; e < ROWS * N; e += 2 * NT) {
+  static_assert((ROWS * N) % (2 * NT) == 0, "whole iterations");
+#pragma unroll
+  for (int it = 0; it < (ROWS * N) / (2 * NT); ++it) {
+    const int e = 2 * tid + it * 2 * NT;
     const int sub = e / N, pos = e % N;
     if (row0 + sub < total_rows) {
       const ModInfo& m = mods[limb_begin + (uint32_t)((row0 + sub) % num_limbs)];
@@ -355,11 +364,23 @@ __global__ __launch_bounds__(ColCfg<LOGN1>::NT) void ntt_col_kernel(uint64_t* da
   uint64_t* base = data + row * N + c0;
   const uint64_t* src = in + row * N + c0;
 
-  for (int e = 2 * tid; e < kCols * N1; e += 2 * NT) {
+  // Every load of the tile is issued before the first LDS write, so that their
+  // latencies overlap.
+  constexpr int kLoads = (kCols * N1) / (2 * NT);
+  static_assert((kCols * N1) % (2 * NT) == 0, "whole iterations");
+  ulonglong2 buf[kLoads];
+#pragma unroll
+  for (int it = 0; it < kLoads; ++it) {
+    const int e = 2 * tid + it * 2 * NT;
     const int rr = e / kCols, c = e % kCols;
-    const ulonglong2 v = *reinterpret_cast<const ulonglong2*>(src + (size_t)rr * N2 + c);
-    lds[c * STRIDE + lpos<A>(rr)] = (T)v.x;
-    lds[(c + 1) * STRIDE + lpos<A>(rr)] = (T)v.y;
+    buf[it] = *reinterpret_cast<const ulonglong2*>(src + (size_t)rr * N2 + c);
+  }
+#pragma unroll
+  for (int it = 0; it < kLoads; ++it) {
+    const int e = 2 * tid + it * 2 * NT;
+    const int rr = e / kCols, c = e % kCols;
+    lds[c * STRIDE + lpos<A>(rr)] = (T)buf[it].x;
+    lds[(c + 1) * STRIDE + lpos<A>(rr)] = (T)buf[it].y;
   }
   __syncthreads();
 
@@ -371,7 +392,10 @@ __global__ __launch_bounds__(ColCfg<LOGN1>::NT) void ntt_col_kernel(uint64_t* da
   auto get_sub = [&](int) { return sp; };
   run_passes<A, FWD, LOGN1, kCols, NT, 0>(lds, tid, get_sub);
 
-  for (int e = 2 * tid; e < kCols * N1; e += 2 * NT) {
+  static_assert((kCols * N1) % (2 * NT) == 0, "whole iterations");
+#pragma unroll
+  for (int it = 0; it < (kCols * N1) / (2 * NT); ++it) {
+    const int e = 2 * tid + it * 2 * NT;
     const int rr = e / kCols, c = e % kCols;
     ulonglong2 v;
     if (LAST) {
@@ -407,11 +431,17 @@ __global__ __launch_bounds__(RowCfg<LOGN2>::NT) void ntt_row_kernel(uint64_t* __
   const uint32_t limb = pl.limb;
   uint64_t* base = data + row * N + (size_t)r0 * N2;
 
-  for (int e = 2 * tid; e < kRows * N2; e += 2 * NT) {
+  constexpr int kLoads = (kRows * N2) / (2 * NT);
+  static_assert((kRows * N2) % (2 * NT) == 0, "whole iterations");
+  ulonglong2 buf[kLoads];
+#pragma unroll
+  for (int it = 0; it < kLoads; ++it) buf[it] = *reinterpret_cast<const ulonglong2*>(base + 2 * tid + it * 2 * NT);
+#pragma unroll
+  for (int it = 0; it < kLoads; ++it) {
+    const int e = 2 * tid + it * 2 * NT;
     const int sub = e / N2, pos = e % N2;
-    const ulonglong2 v = *reinterpret_cast<const ulonglong2*>(base + e);
-    lds[sub * STRIDE + lpos<A>(pos)] = (T)v.x;
-    lds[sub * STRIDE + lpos<A>(pos + 1)] = (T)v.y;
+    lds[sub * STRIDE + lpos<A>(pos)] = (T)buf[it].x;
+    lds[sub * STRIDE + lpos<A>(pos + 1)] = (T)buf[it].y;
   }
   __syncthreads();
 
@@ -427,7 +457,10 @@ __global__ __launch_bounds__(RowCfg<LOGN2>::NT) void ntt_row_kernel(uint64_t* __
   };
   run_passes<A, FWD, LOGN2, kRows, NT, 0>(lds, tid, get_sub);
 
-  for (int e = 2 * tid; e < kRows * N2; e += 2 * NT) {
+  static_assert((kRows * N2) % (2 * NT) == 0, "whole iterations");
+#pragma unroll
+  for (int it = 0; it < (kRows * N2) / (2 * NT); ++it) {
+    const int e = 2 * tid + it * 2 * NT;
     const int sub = e / N2, pos = e % N2;
     ulonglong2 v;
     if (GAL) {
