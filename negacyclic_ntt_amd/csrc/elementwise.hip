@@ -254,8 +254,12 @@ hipError_t launch_rescale(const ntt_plan* p, uint64_t* out, const uint64_t* in, 
   const uint32_t tiles = (p->n / 2 + kThreads - 1) / kThreads;
   // Enough blocks to fill the chip: split the output limbs into groups when the
   // batch is small (each group re-reads the dropped limb, one row of n words).
+#ifndef NNTT_RESCALE_BLOCKS
+#define NNTT_RESCALE_BLOCKS 2048
+#endif
   const uint64_t base = (uint64_t)tiles * batch;
-  const uint32_t want = (uint32_t)std::min<uint64_t>(num_limbs - 1, (2048 + base - 1) / base);
+  const uint32_t want =
+      (uint32_t)std::min<uint64_t>(num_limbs - 1, (NNTT_RESCALE_BLOCKS + base - 1) / base);
   const uint32_t groups = std::max(1u, want);
   for (uint64_t b0 = 0; b0 < batch; b0 += 65535) {
     const uint64_t nb = std::min<uint64_t>(65535, batch - b0);

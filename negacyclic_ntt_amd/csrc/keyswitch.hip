@@ -135,13 +135,30 @@ __device__ __forceinline__ uint64_t dot30(const uint32_t (&vl)[K], const uint32_
   return r;
 }
 
-template <int K>
-__device__ __forceinline__ void split30(const uint64_t (&v)[K], uint32_t (&vl)[K], uint32_t (&vh)[K], uint32_t k) {
+// Garner digits below 2^60 with each inner sum s_i = sum_{k<i} v_k g_ik as a 30-bit
+// half dot product (constants g30[i S + k] = g_ik 2^64 mod m_i, one Montgomery
+// reduction), then v_i = (x_i + m_i - s_i) g_ii mod m_i by a Shoup product.  Also
+// returns the halves of every digit for the evaluations that follow.
+template <int K, int S>
+__device__ __forceinline__ void garner30(const uint64_t (&x)[K], uint64_t (&v)[K], uint32_t (&vl)[K],
+                                         uint32_t (&vh)[K], uint32_t k, const uint64_t* __restrict__ m,
+                                         const uint64_t* __restrict__ ninv, const Tw* __restrict__ g,
+                                         const C30* __restrict__ g30) {
+  static_assert(K <= S, "register width exceeds the table stride");
 #pragma unroll
   for (int i = 0; i < K; ++i) {
     if (i >= (int)k) break;
-    vl[i] = (uint32_t)v[i] & 0x3fffffffu;
-    vh[i] = (uint32_t)(v[i] >> 30);
+    uint64_t vi;
+    if (i == 0) {
+      vi = x[0];
+    } else {
+      const uint64_t mi = m[i];
+      const uint64_t si = dot30<K>(vl, vh, (uint32_t)i, g30 + i * S, mi, ninv[i]);
+      vi = csub(shoup<true>(x[i] + mi - si, g[i * S + i], mi), mi);  // x_i + m_i - s_i < 2 m_i
+    }
+    v[i] = vi;
+    vl[i] = (uint32_t)vi & 0x3fffffffu;
+    vh[i] = (uint32_t)(vi >> 30);
   }
 }
 
@@ -168,6 +185,8 @@ struct KsDev {
   const Tw* r_scale;        // [nq+np]  2^64 mod q_t
   const C30* digit_eval30;  // [dnum][nq+np][K]  below 2^60: digit products times 2^128 mod q_t
   const C30* p_eval30;      // [nq][KP]           below 2^60: products of P's primes times 2^64
+  const C30* digit_garner30;  // [dnum][K][K]     below 2^60: Garner constants times 2^64 (k < i)
+  const C30* p_garner30;      // [KP][KP]
   const uint64_t* ninv;     // [nq+np]  -q_t^-1 mod 2^64
 };
 
@@ -212,14 +231,17 @@ __global__ __launch_bounds__(kKsThreads) void modup_kernel(uint64_t* __restrict_
     }
   }
   constexpr int S = kMaxDigitPrimes;
-  garner<B60, K, S>(x, v, alpha, kc.moduli + first, kc.digit_garner + (size_t)j * S * S);
+  uint32_t vl[K], vh[K];
+  if constexpr (B60)
+    garner30<K, S>(x, v, vl, vh, alpha, kc.moduli + first, kc.ninv + first, kc.digit_garner + (size_t)j * S * S,
+                   kc.digit_garner30 + (size_t)j * S * S);
+  else
+    garner<B60, K, S>(x, v, alpha, kc.moduli + first, kc.digit_garner + (size_t)j * S * S);
   const Tw* ev = kc.digit_eval + (size_t)j * nqp * S;
   // targets m = 0 .. nqp - alpha - 1 skip the digit's own primes: t = m or m + alpha
   const uint32_t others = nqp - alpha, per = (others + gridDim.z - 1) / gridDim.z;
   const uint32_t m0 = blockIdx.z * per, m1 = min(others, m0 + per);
   if constexpr (B60) {
-    uint32_t vl[K], vh[K];
-    split30<K>(v, vl, vh, alpha);
     const C30* ev30 = kc.digit_eval30 + (size_t)j * nqp * S;
 #pragma unroll 2
     for (uint32_t m = m0; m < m1; ++m) {
@@ -397,15 +419,17 @@ __global__ __launch_bounds__(kKsThreads) void moddown_kernel(uint64_t* __restric
     y[i] = a[(uint64_t)(nq + i) * n];
   }
   constexpr int S = kMaxSpecial;
-  garner<B60, KP, S>(y, v, np_, kc.moduli + nq, kc.p_garner);
+  uint32_t vl[KP], vh[KP];
+  if constexpr (B60)
+    garner30<KP, S>(y, v, vl, vh, np_, kc.moduli + nq, kc.ninv + nq, kc.p_garner, kc.p_garner30);
+  else
+    garner<B60, KP, S>(y, v, np_, kc.moduli + nq, kc.p_garner);
   const bool adds = (add_mask >> comp) & 1u;
   const uint64_t* c0 = add + (uint64_t)b * add_stride + (uint64_t)comp * nq * n;
   const Gather gi = gather_index(e, h, logn);
   uint64_t* o = out + (uint64_t)bc * nq * n + e;
   const uint32_t per = (nq + groups - 1) / groups;
   const uint32_t l0 = grp * per, l1 = min(nq, l0 + per);
-  uint32_t vl[KP], vh[KP];
-  if constexpr (B60) split30<KP>(v, vl, vh, np_);
 #pragma unroll 4
   for (uint32_t l = l0; l < l1; ++l) {
     const uint64_t q = kc.moduli[l];
@@ -536,13 +560,25 @@ extern "C" int keyswitch_plan_create(ntt_ks_plan** out, const ntt_plan* qp, uint
   std::vector<uint64_t> ninv(nqp);
   auto split = [](uint64_t c) { return C30{(uint32_t)(c & 0x3fffffffu), (uint32_t)(c >> 30)}; };
   for (uint32_t t = 0; t < nqp; ++t) ninv[t] = qp->h_mods[t].mont_ninv;
+  std::vector<C30> dg30((size_t)dnum * K * K, C30{0, 0}), pg30((size_t)KP * KP, C30{0, 0});
   if (range_below60(qp, 0, nqp)) {
     for (size_t i = 0; i < de30.size(); ++i) {
       const uint32_t t = (uint32_t)((i / K) % nqp);
       de30[i] = split(host_mulmod(de[i].w, rs[t].w, m[t]));
     }
+    for (uint32_t j = 0; j < dnum; ++j)  // below-diagonal Garner constants of digit j, times 2^64
+      for (uint32_t i = 1; i < alpha; ++i)
+        for (uint32_t kk = 0; kk < i; ++kk) {
+          const size_t idx = ((size_t)j * K + i) * K + kk;
+          const uint32_t t = j * alpha + i;
+          dg30[idx] = split(host_mulmod(dg[idx].w, rs[t].w, m[t]));
+        }
   }
   garner_table(m + nq, np_, KP, pg.data());
+  if (range_below60(qp, 0, nqp))
+    for (uint32_t i = 1; i < np_; ++i)
+      for (uint32_t kk = 0; kk < i; ++kk)
+        pg30[(size_t)i * KP + kk] = split(host_mulmod(pg[(size_t)i * KP + kk].w, rs[nq + i].w, m[nq + i]));
   for (uint32_t l = 0; l < nq; ++l) {
     eval_table(m + nq, np_, m[l], pe.data() + (size_t)l * KP);
     if (range_below60(qp, 0, nqp))
@@ -556,12 +592,12 @@ extern "C" int keyswitch_plan_create(ntt_ks_plan** out, const ntt_plan* qp, uint
   const size_t sz_m = moduli.size() * 8, sz_dg = dg.size() * sizeof(Tw), sz_de = de.size() * sizeof(Tw);
   const size_t sz_pg = pg.size() * sizeof(Tw), sz_pe = pe.size() * sizeof(Tw), sz_pi = pinv.size() * sizeof(Tw);
   const size_t sz_rs = rs.size() * sizeof(Tw), sz_d30 = de30.size() * sizeof(C30), sz_p30 = pe30.size() * sizeof(C30);
-  const size_t sz_ni = ninv.size() * 8;
+  const size_t sz_ni = ninv.size() * 8, sz_dg30 = dg30.size() * sizeof(C30), sz_pg30 = pg30.size() * sizeof(C30);
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  constexpr int kParts = 10;
-  const void* src[kParts] = {moduli.data(), dg.data(), de.data(),   pg.data(),   pe.data(),
-                             pinv.data(),   rs.data(), de30.data(), pe30.data(), ninv.data()};
-  const size_t sz[kParts] = {sz_m, sz_dg, sz_de, sz_pg, sz_pe, sz_pi, sz_rs, sz_d30, sz_p30, sz_ni};
+  constexpr int kParts = 12;
+  const void* src[kParts] = {moduli.data(), dg.data(),   de.data(),   pg.data(), pe.data(),   pinv.data(),
+                             rs.data(),     de30.data(), pe30.data(), ninv.data(), dg30.data(), pg30.data()};
+  const size_t sz[kParts] = {sz_m, sz_dg, sz_de, sz_pg, sz_pe, sz_pi, sz_rs, sz_d30, sz_p30, sz_ni, sz_dg30, sz_pg30};
   size_t total = 0;
   for (int i = 0; i < kParts; ++i) total += al(sz[i]);
   std::vector<uint8_t> blob(total, 0);
@@ -607,6 +643,8 @@ extern "C" int keyswitch_plan_create(ntt_ks_plan** out, const ntt_plan* qp, uint
   p->dev.digit_eval30 = (const C30*)(base + off[7]);
   p->dev.p_eval30 = (const C30*)(base + off[8]);
   p->dev.ninv = (const uint64_t*)(base + off[9]);
+  p->dev.digit_garner30 = (const C30*)(base + off[10]);
+  p->dev.p_garner30 = (const C30*)(base + off[11]);
   p->mac_chunk = (uint32_t)std::min<uint64_t>(dnum, ~0ull / qmax);
   *out = p;
   return NTT_OK;
