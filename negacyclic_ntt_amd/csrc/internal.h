@@ -76,6 +76,12 @@ hipError_t launch_ntt(const ntt_plan* p, uint64_t* data, uint64_t batch, uint32_
                       bool inverse, hipStream_t s);
 hipError_t launch_ntt_galois(const ntt_plan* p, uint64_t* out, const uint64_t* in, uint64_t g, uint64_t batch,
                              uint32_t limb_begin, uint32_t num_limbs, hipStream_t s);
+// Key product fused into the inverse transform (two-pass sizes, n >= 2^15): acc
+// [batch][2][nqp][n] = INTT( sum_j ext[b][j] * ksk[j][c] ) with the digits ext in
+// Montgomery form (times 2^64) and `chunk` products summed per reduction.
+bool intt_mac_supported(const ntt_plan* p);
+hipError_t launch_intt_mac(const ntt_plan* p, uint64_t* acc, const uint64_t* ext, const uint64_t* ksk, uint64_t batch,
+                           uint32_t nqp, uint32_t dnum, uint32_t chunk, hipStream_t s);
 // True when every prime in [limb_begin, limb_begin + num_limbs) is below 2^30.
 bool range_is_narrow(const ntt_plan* p, uint32_t limb_begin, uint32_t num_limbs);
 // True when every prime in the range is below 2^60.

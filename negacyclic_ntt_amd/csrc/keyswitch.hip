@@ -789,6 +789,12 @@ int ks_run(const ntt_ks_plan* p, uint64_t* out, const KsIo& io, const uint64_t* 
   int rc = ks_modup(p, ext, io, h, batch, s);
   if (rc) return rc;
   if (launch_ntt(qp, ext, batch * dnum, 0, nqp, false, s) != hipSuccess) return NTT_EDEVICE;
+  if (intt_mac_supported(qp)) {  // key product fused into the inverse transform's first pass
+    if (launch_intt_mac(qp, acc, ext, ksk, batch, nqp, dnum, p->mac_chunk, s) != hipSuccess) return NTT_EDEVICE;
+    HoistArgs ha{};
+    ha.h[0] = h;
+    return ks_moddown(p, out, acc, io, ha, 1, batch, s);
+  }
   const uint64_t pairs = (uint64_t)nqp * n / 2;
   for (uint64_t b0 = 0; b0 < batch; b0 += kMaxGridY) {
     const uint64_t nb = std::min(kMaxGridY, batch - b0);

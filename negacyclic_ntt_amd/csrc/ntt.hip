@@ -480,6 +480,109 @@ __global__ __launch_bounds__(RowCfg<LOGN2>::NT) void ntt_row_kernel(uint64_t* __
   }
 }
 
+// The key product of the key-switch fused into the inverse transform's first (row)
+// pass.  Tensor row poly * nqp + t of the accumulator, poly = 2 b + c, is
+//   acc = sum_j ext[b][j][t] * ksk[j][c][t]   (mod q_t)
+// computed as it is loaded: the digits are in Montgomery form (times 2^64), so the
+// exact 128-bit sum of up to `chunk` products is reduced once per chunk.  The rest is
+// the ordinary Gentleman-Sande row pass; the column pass follows unchanged.
+struct MacSrc {
+  const uint64_t* ext;  // [batch][dnum][nqp][n]
+  const uint64_t* ksk;  // [dnum][2][nqp][n]
+  uint32_t dnum, chunk;
+};
+
+// DN > 0: dnum == DN and DN products fit one reduction (all loads of an element pair
+// are issued before any arithmetic); DN == 0: any dnum, chunked reductions.
+template <class A, int LOGN1, int LOGN2, int DN>
+__global__ __launch_bounds__(RowCfg<LOGN2>::NT) void ntt_row_mac_kernel(uint64_t* __restrict__ acc, MacSrc ms,
+                                                                        const void* __restrict__ tw_all,
+                                                                        const ModInfo* __restrict__ mods,
+                                                                        uint32_t nqp, uint64_t polys) {
+  using T = typename A::T;
+  constexpr int N1 = 1 << LOGN1, N2 = 1 << LOGN2, N = N1 * N2;
+  constexpr int NT = RowCfg<LOGN2>::NT;
+  constexpr int STRIDE = sub_stride<A>(LOGN2);
+  constexpr int BLOCKS_PER_LIMB = N1 / kRows;
+  __shared__ T lds[kRows * STRIDE];
+  const int tid = threadIdx.x;
+  const Place pl = place_block(BLOCKS_PER_LIMB, polys, nqp, 0);
+  const uint64_t row = pl.row, poly = row / nqp;
+  const uint32_t t = pl.limb;
+  const size_t off = (size_t)pl.tile * kRows * N2;  // first element of this tile in the limb
+  const uint64_t plane = (uint64_t)nqp * N;
+  const uint64_t* xe = ms.ext + ((poly >> 1) * ms.dnum * nqp + t) * (uint64_t)N + off;
+  const uint64_t* kk = ms.ksk + ((poly & 1) * nqp + t) * (uint64_t)N + off;
+  const ModInfo& m = mods[t];
+  const uint64_t q = m.q, ninv = m.mont_ninv;
+
+  constexpr int kIters = (kRows * N2) / (2 * NT);
+  static_assert((kRows * N2) % (2 * NT) == 0, "whole iterations");
+#pragma unroll 2
+  for (int it = 0; it < kIters; ++it) {
+    const int e = 2 * tid + it * 2 * NT;
+    Acc128 a0{0, 0}, a1{0, 0};
+    uint64_t r0 = 0, r1 = 0;
+    if constexpr (DN > 0) {
+      ulonglong2 d[DN], k[DN];
+#pragma unroll
+      for (int j = 0; j < DN; ++j) {
+        d[j] = *reinterpret_cast<const ulonglong2*>(xe + j * plane + e);
+        k[j] = *reinterpret_cast<const ulonglong2*>(kk + 2 * j * plane + e);
+      }
+#pragma unroll
+      for (int j = 0; j < DN; ++j) {
+        mac128(a0, d[j].x, k[j].x);
+        mac128(a1, d[j].y, k[j].y);
+      }
+      r0 = csub(redc(a0, q, ninv), q);
+      r1 = csub(redc(a1, q, ninv), q);
+    } else {
+    uint32_t c = 0;
+    for (uint32_t j = 0; j < ms.dnum; ++j) {
+      const ulonglong2 d = *reinterpret_cast<const ulonglong2*>(xe + j * plane + e);
+      const ulonglong2 k = *reinterpret_cast<const ulonglong2*>(kk + 2 * j * plane + e);
+      mac128(a0, d.x, k.x);
+      mac128(a1, d.y, k.y);
+      if (++c == ms.chunk || j + 1 == ms.dnum) {
+        r0 = add_mod(r0, csub(redc(a0, q, ninv), q), q);
+        r1 = add_mod(r1, csub(redc(a1, q, ninv), q), q);
+        a0 = Acc128{0, 0};
+        a1 = Acc128{0, 0};
+        c = 0;
+      }
+    }
+    }
+    const int sub = e / N2, pos = e % N2;
+    lds[sub * STRIDE + lpos<A>(pos)] = (T)r0;
+    lds[sub * STRIDE + lpos<A>(pos + 1)] = (T)r1;
+  }
+  __syncthreads();
+
+  const typename A::Tw* tw = table_of<A>(tw_all, t, N);
+  const T qt = modulus<A>(m);
+  auto get_sub = [&](int sub) {
+    SubParams<A> sp;
+    sp.tw = tw;
+    sp.q = qt;
+    sp.prefix = (uint32_t)N1 + (uint32_t)(pl.tile * kRows + sub);
+    return sp;
+  };
+  run_passes<A, false, LOGN2, kRows, NT, 0>(lds, tid, get_sub);
+
+  uint64_t* base = acc + row * N + off;
+  static_assert((kRows * N2) % (2 * NT) == 0, "whole iterations");
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
+    const int e = 2 * tid + it * 2 * NT;
+    const int sub = e / N2, pos = e % N2;
+    ulonglong2 v;
+    v.x = A::widen(lds[sub * STRIDE + lpos<A>(pos)]);
+    v.y = A::widen(lds[sub * STRIDE + lpos<A>(pos + 1)]);
+    *reinterpret_cast<ulonglong2*>(base + e) = v;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // What one launch sequence computes.
 enum class Op { kForward, kInverse, kForwardGalois };
@@ -537,6 +640,35 @@ hipError_t launch_split(const ntt_plan* p, uint64_t* data, const uint64_t* in, u
                        tw, p->d_mods, num_limbs, limb_begin, batch, 1u);
   }
   return hipGetLastError();
+}
+
+template <class A, int LOGN1, int LOGN2>
+hipError_t launch_mac_split(const ntt_plan* p, uint64_t* acc, const MacSrc& ms, uint64_t batch, uint32_t nqp,
+                            hipStream_t s) {
+  const void* tw = tables_for<A>(p, Op::kInverse);
+  const uint64_t polys = 2 * batch, rows = polys * nqp;
+  const dim3 col_grid((uint32_t)(rows * ((1u << LOGN2) / kCols))), col_block(ColCfg<LOGN1>::NT);
+  const dim3 row_grid((uint32_t)(rows * ((1u << LOGN1) / kRows))), row_block(RowCfg<LOGN2>::NT);
+  const bool one = ms.dnum <= ms.chunk;  // a single reduction covers every digit
+#define NNTT_MAC_ROW(D) \
+  hipLaunchKernelGGL((ntt_row_mac_kernel<A, LOGN1, LOGN2, D>), row_grid, row_block, 0, s, acc, ms, tw, p->d_mods, nqp, polys)
+  if (one && ms.dnum == 1) NNTT_MAC_ROW(1);
+  else if (one && ms.dnum == 2) NNTT_MAC_ROW(2);
+  else if (one && ms.dnum == 3) NNTT_MAC_ROW(3);
+  else if (one && ms.dnum == 4) NNTT_MAC_ROW(4);
+  else NNTT_MAC_ROW(0);
+#undef NNTT_MAC_ROW
+  hipLaunchKernelGGL((ntt_col_kernel<A, LOGN1, LOGN2, false, true, false>), col_grid, col_block, 0, s, acc, acc, tw,
+                     p->d_mods, nqp, 0u, polys, 1u);
+  return hipGetLastError();
+}
+
+template <class A>
+hipError_t launch_mac_any(const ntt_plan* p, uint64_t* acc, const MacSrc& ms, uint64_t batch, uint32_t nqp,
+                          hipStream_t s) {
+  if (p->logn == 15) return launch_mac_split<A, 7, 8>(p, acc, ms, batch, nqp, s);
+  if (p->logn == 16) return launch_mac_split<A, 8, 8>(p, acc, ms, batch, nqp, s);
+  return hipErrorNotSupported;
 }
 
 template <class A>
@@ -598,6 +730,18 @@ bool range_below60(const ntt_plan* p, uint32_t limb_begin, uint32_t num_limbs) {
 hipError_t launch_ntt(const ntt_plan* p, uint64_t* data, uint64_t batch, uint32_t limb_begin, uint32_t num_limbs,
                       bool inverse, hipStream_t s) {
   return dispatch(p, data, data, batch, limb_begin, num_limbs, inverse ? Op::kInverse : Op::kForward, 1u, s);
+}
+
+bool intt_mac_supported(const ntt_plan* p) { return p->logn >= 15; }
+
+hipError_t launch_intt_mac(const ntt_plan* p, uint64_t* acc, const uint64_t* ext, const uint64_t* ksk, uint64_t batch,
+                           uint32_t nqp, uint32_t dnum, uint32_t chunk, hipStream_t s) {
+  if (!intt_mac_supported(p)) return hipErrorNotSupported;
+  if (batch == 0) return hipSuccess;
+  const MacSrc ms{ext, ksk, dnum, chunk};
+  if (range_is_narrow(p, 0, nqp)) return launch_mac_any<Narrow>(p, acc, ms, batch, nqp, s);
+  if (range_below60(p, 0, nqp)) return launch_mac_any<Wide60>(p, acc, ms, batch, nqp, s);
+  return launch_mac_any<Wide>(p, acc, ms, batch, nqp, s);
 }
 
 hipError_t launch_ntt_galois(const ntt_plan* p, uint64_t* out, const uint64_t* in, uint64_t g, uint64_t batch,

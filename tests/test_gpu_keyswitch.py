@@ -49,6 +49,25 @@ def test_keyswitch_shapes_vs_oracle(B, logn, nq, npr, dnum):
     assert_bits_equal(host(out), orc.keyswitch(ct, ksk, g, qp[: nq + npr], nq, dnum), "keyswitch shape")
 
 
+@pytest.mark.parametrize("logn,bits,nq,npr,dnum", [(15, 60, 12, 4, 3), (15, 60, 10, 2, 5), (15, 62, 12, 4, 3),
+                                                   (15, 62, 10, 3, 5), (16, 62, 8, 2, 4), (15, 30, 6, 2, 2)])
+def test_keyswitch_fused_product_paths(B, logn, bits, nq, npr, dnum):
+    """Two-pass ring sizes, where the key product runs inside the inverse transform:
+    both splits (2^15 = 2^7 x 2^8, 2^16), compile-time digit counts and the runtime
+    loop (dnum 5), 60-bit (one reduction) and 62-bit primes (four products per
+    reduction, so five digits take two), and 30-bit primes."""
+    n = 1 << logn
+    qp = list(primes(bits, 2 * n, nq + npr))
+    plan = B.Plan(n, qp, 0)
+    ks = B.KeySwitchPlan(plan, nq, npr, dnum)
+    ct = residues((2, 2, nq, n), qp[:nq], 9800 + logn + bits + dnum)
+    ksk = residues((dnum, 2, nq + npr, n), qp, 9900 + logn + bits + dnum)
+    g = 25
+    announce("keyswitch fused product", logn, bits, nq, npr, dnum)
+    out = B.keyswitch(ks, dev(np.zeros_like(ct)), dev(ct), dev(ksk), g)
+    assert_bits_equal(host(out), orc.keyswitch(ct, ksk, g, qp, nq, dnum), "keyswitch fused product")
+
+
 def test_keyswitch_zero_key_and_zero_c1(B):
     n = 1 << 12
     qp, plan, ks = _setup(B, n)

@@ -137,6 +137,16 @@ def test_relinearize_shapes_vs_oracle(B, logn, nq, npr, dnum, batch):
                       "relinearize shape")
 
 
+def test_relinearize_two_pass_ring(B):
+    """n = 2^15 (the 2^7 x 2^8 split with the key product inside the inverse transform), batch 2."""
+    n = 1 << 15
+    qp, plan, ks = _ks_setup(B, n, 12, 4, 3)
+    d = residues((2, 3, 12, n), qp[:12], 7450)
+    rlk = residues((3, 2, 16, n), qp[:16], 7451)
+    announce("relinearize 2^15")
+    assert_bits_equal(_relin_gpu(B, ks, d, rlk), orc.relinearize(d, rlk, qp[:16], 12, 3), "relinearize 2^15")
+
+
 def test_relinearize_zero_key_and_zero_d2(B):
     n = 1 << 12
     qp, plan, ks = _ks_setup(B, n)
