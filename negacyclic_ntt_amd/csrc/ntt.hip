@@ -61,6 +61,9 @@ constexpr Sched make_sched(int logm) {
   return S;
 }
 
+#ifndef NNTT_COL_TW_LDS
+#define NNTT_COL_TW_LDS 1  // measured on MI355X: forward 2^16 NTT 2.5% faster
+#endif
 #ifndef NNTT_LDS_PAD
 #define NNTT_LDS_PAD 1
 #endif
@@ -386,7 +389,18 @@ __global__ __launch_bounds__(ColCfg<LOGN1>::NT) void ntt_col_kernel(uint64_t* da
 
   const ModInfo& m = mods[limb];
   SubParams<A> sp;
+#if NNTT_COL_TW_LDS
+  // A column transform (prefix 1) uses table entries below N1 only: stage them in LDS.
+  __shared__ typename A::Tw tw_lds[N1];
+  {
+    const typename A::Tw* tg = table_of<A>(tw_all, limb, N);
+    for (int i = tid; i < N1; i += NT) tw_lds[i] = tg[i];
+  }
+  __syncthreads();
+  sp.tw = tw_lds;
+#else
   sp.tw = table_of<A>(tw_all, limb, N);
+#endif
   sp.q = modulus<A>(m);
   sp.prefix = 1;
   auto get_sub = [&](int) { return sp; };
