@@ -61,6 +61,9 @@ constexpr Sched make_sched(int logm) {
   return S;
 }
 
+#ifndef NNTT_ROW_FWD_PRELOAD
+#define NNTT_ROW_FWD_PRELOAD 0
+#endif
 #ifndef NNTT_COL_TW_LDS
 #define NNTT_COL_TW_LDS 1  // measured on MI355X: forward 2^16 NTT 2.5% faster
 #endif
@@ -115,7 +118,7 @@ struct SubParams {
 
 // One pass: radix 2^R sets over stages [S0, S0 + R) of every sub-transform held
 // in LDS.  NSUB sub-transforms of size 2^LOGM, NT threads.
-template <class A, bool FWD, int LOGM, int R, int S0, int NSUB, int NT, class GetSub>
+template <class A, bool FWD, int LOGM, int R, int S0, int NSUB, int NT, bool PRE, class GetSub>
 __device__ __forceinline__ void run_pass(typename A::T* lds, int tid, const GetSub& get_sub) {
   using T = typename A::T;
   constexpr int M = 1 << LOGM;
@@ -136,7 +139,25 @@ __device__ __forceinline__ void run_pass(typename A::T* lds, int tid, const GetS
     const T q = sp.q, two_q = q + q;
     const uint32_t pg = (sp.prefix << S0) + (uint32_t)g;
     T x[1 << R];
-    if (FWD) {
+    if (FWD && PRE) {
+      // Forward with every twiddle of the set requested before the LDS reads.
+      typename A::Tw wv[(1 << R) - 1];
+#pragma unroll
+      for (int v = 0; v < R; ++v)
+#pragma unroll
+        for (int j = 0; j < (1 << v); ++j) wv[(1 << v) - 1 + j] = sp.tw[(pg << v) + (uint32_t)j];
+#pragma unroll
+      for (int i = 0; i < (1 << R); ++i) x[i] = base[lpos<A>(pos0 + i * TP)];
+#pragma unroll
+      for (int v = 0; v < R; ++v) {
+        const int half = 1 << (R - 1 - v);
+#pragma unroll
+        for (int i = 0; i < (1 << R); ++i) {
+          if (i & half) continue;
+          ct_butterfly<A>(x[i], x[i + half], wv[(1 << v) - 1 + (i >> (R - v))], q, two_q);
+        }
+      }
+    } else if (FWD) {
 #pragma unroll
       for (int i = 0; i < (1 << R); ++i) x[i] = base[lpos<A>(pos0 + i * TP)];
 #pragma unroll
@@ -178,14 +199,14 @@ __device__ __forceinline__ void run_pass(typename A::T* lds, int tid, const GetS
 
 // All passes of a sub-transform of size 2^LOGM, forward (sigma up) or inverse
 // (sigma down).  Ends with a barrier.
-template <class A, bool FWD, int LOGM, int NSUB, int NT, int P, class GetSub>
+template <class A, bool FWD, int LOGM, int NSUB, int NT, int P, class GetSub, bool PRE = false>
 __device__ __forceinline__ void run_passes(typename A::T* lds, int tid, const GetSub& get_sub) {
   constexpr Sched S = make_sched(LOGM);
   if constexpr (P < S.np) {
     constexpr int idx = FWD ? P : S.np - 1 - P;
-    run_pass<A, FWD, LOGM, S.r[idx], S.s[idx], NSUB, NT>(lds, tid, get_sub);
+    run_pass<A, FWD, LOGM, S.r[idx], S.s[idx], NSUB, NT, PRE>(lds, tid, get_sub);
     __syncthreads();
-    run_passes<A, FWD, LOGM, NSUB, NT, P + 1>(lds, tid, get_sub);
+    run_passes<A, FWD, LOGM, NSUB, NT, P + 1, GetSub, PRE>(lds, tid, get_sub);
   }
 }
 
@@ -469,7 +490,7 @@ __global__ __launch_bounds__(RowCfg<LOGN2>::NT) void ntt_row_kernel(uint64_t* __
     sp.prefix = (uint32_t)N1 + (GAL ? galois_row<LOGN1>((uint32_t)(r0 + sub), galois) : (uint32_t)(r0 + sub));
     return sp;
   };
-  run_passes<A, FWD, LOGN2, kRows, NT, 0>(lds, tid, get_sub);
+  run_passes<A, FWD, LOGN2, kRows, NT, 0, decltype(get_sub), NNTT_ROW_FWD_PRELOAD != 0>(lds, tid, get_sub);
 
   static_assert((kRows * N2) % (2 * NT) == 0, "whole iterations");
 #pragma unroll
