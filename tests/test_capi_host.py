@@ -127,8 +127,27 @@ def test_compute_calls_reject_host_plans_and_bad_args():
     assert L.ntt_forward(None, fake, 1, 0, 2, None) == B.NTT_EINVAL
     # keyswitch plans need a device plan
     h = ctypes.c_void_p()
-    assert L.keyswitch_plan_create(ctypes.byref(h), plan.handle, 1, 1, 1) != B.NTT_OK
-    assert L.keyswitch_plan_create(ctypes.byref(h), None, 1, 1, 1) != B.NTT_OK
+    assert L.keyswitch_plan_create(ctypes.byref(h), plan.handle, 1, 1, 1) == B.NTT_EDEVICE
+    assert L.keyswitch_plan_create(ctypes.byref(h), None, 1, 1, 1) == B.NTT_EINVAL
+    assert L.keyswitch_plan_create(None, plan.handle, 1, 1, 1) == B.NTT_EINVAL
+    # rescale: host plan, then argument errors that need no device
+    assert L.rescale(plan.handle, fake, fake, 0, 1, 0, 2, None) == B.NTT_EDEVICE
+    assert L.rescale(None, fake, fake, 0, 1, 0, 2, None) == B.NTT_EINVAL
+    # modraise plans need a device plan
+    assert L.modraise_plan_create(ctypes.byref(h), plan.handle, 1, 2) == B.NTT_EDEVICE
+    assert L.modraise_plan_create(ctypes.byref(h), None, 1, 2) == B.NTT_EINVAL
+    assert L.modraise_plan_create(None, plan.handle, 1, 2) == B.NTT_EINVAL
+    # every entry point taking a key-switch / modraise plan rejects a null plan
+    g = (ctypes.c_uint64 * 1)(5)
+    sz = ctypes.c_size_t()
+    assert L.keyswitch(None, fake, fake, fake, 5, 1, fake, 1 << 30, None) == B.NTT_EINVAL
+    assert L.relinearize(None, fake, fake, fake, 1, fake, 1 << 30, None) == B.NTT_EINVAL
+    assert L.keyswitch_hoisted(None, fake, fake, fake, g, 1, 1, fake, 1 << 30, None) == B.NTT_EINVAL
+    assert L.keyswitch_workspace_size(None, 1, ctypes.byref(sz)) == B.NTT_EINVAL
+    assert L.keyswitch_hoisted_workspace_size(None, 1, 1, ctypes.byref(sz)) == B.NTT_EINVAL
+    assert L.modraise(None, fake, fake, 1, None) == B.NTT_EINVAL
+    L.keyswitch_plan_destroy(None)  # null is a no-op
+    L.modraise_plan_destroy(None)
 
 
 def test_plan_info():
