@@ -166,6 +166,26 @@ int automorph(const ntt_plan *plan, uint64_t *out, const uint64_t *in, uint64_t 
 int rescale(const ntt_plan *plan, uint64_t *out, const uint64_t *in, int mode, uint64_t batch, uint32_t limb_begin,
             uint32_t num_limbs, void *stream);
 
+/* ---- input checks (debugging) -------------------------------------------- */
+
+/* Adds to *count (a device uint64, 8-byte aligned, zeroed by the caller) the number of
+ * residues of data [batch][num_limbs][n] that are not canonical, i.e. >= the plan
+ * prime of their limb (limb_begin + t).  Asynchronous on `stream`.  Every other entry
+ * point assumes canonical inputs (outputs of non-canonical inputs are unspecified
+ * but every access stays in bounds). */
+int ntt_count_noncanonical(const ntt_plan *plan, const uint64_t *data, uint64_t batch, uint32_t limb_begin,
+                           uint32_t num_limbs, uint64_t *count, void *stream);
+
+/* Debug mode (off unless the environment variable NTT_CHECK_INPUTS is set to a value
+ * other than "" or "0"; this call overrides it for the process): every entry point
+ * first counts the non-canonical residues of its inputs -- operands, ciphertexts and
+ * keys -- waits for the count on the caller's stream and returns NTT_EINVAL, having
+ * launched nothing else, if any is found.  The checks synchronise the stream and are
+ * serialised across threads; the FHElium pages ("Eager, Compile, and native
+ * execution", section "Schema registration and device dispatch") validate inputs
+ * before any launch, and this extends that to the values, at a cost. */
+void ntt_set_debug_checks(int on);
+
 /* Key-switch plan over a Q u P basis: the first num_q primes of qp_plan form Q
  * and the next num_p form P (num_q + num_p <= primes in qp_plan); Q is split into
  * dnum digits of num_q / dnum consecutive primes (num_q % dnum == 0,

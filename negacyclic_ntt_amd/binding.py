@@ -61,6 +61,8 @@ def lib():
             "keyswitch_hoisted_workspace_size": (i32, [_VP, u32, u64, ctypes.POINTER(sz)]),
             "keyswitch_hoisted": (i32, [_VP, _VP, _VP, _VP, _U64P, u32, u64, _VP, sz, _VP]),
             "rescale": (i32, [_VP, _VP, _VP, i32, u64, u32, u32, _VP]),
+            "ntt_count_noncanonical": (i32, [_VP, _VP, u64, u32, u32, _VP, _VP]),
+            "ntt_set_debug_checks": (None, [i32]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -221,6 +223,21 @@ def automorph(plan: Plan, out, x, galois_elt: int, domain: int = 0, limb_begin: 
     _check(lib().automorph(plan.handle, _VP(out.data_ptr()), _VP(x.data_ptr()), galois_elt, domain, batch,
                            limb_begin, limbs, _stream_ptr(x, stream)), "automorph")
     return out
+
+
+def count_noncanonical(plan: Plan, x, limb_begin: int = 0, stream=None) -> int:
+    """Number of residues of x [..., limbs, n] that are >= their prime (synchronises)."""
+    import torch
+    batch, limbs = _check_tensor(x, plan, "x")
+    cnt = torch.zeros(1, dtype=torch.int64, device=x.device)
+    _check(lib().ntt_count_noncanonical(plan.handle, _VP(x.data_ptr()), batch, limb_begin, limbs,
+                                        _VP(cnt.data_ptr()), _stream_ptr(x, stream)), "ntt_count_noncanonical")
+    return int(cnt.item())
+
+
+def set_debug_checks(on: bool):
+    """Turn the library's input checks on or off for this process (see ntt_set_debug_checks)."""
+    lib().ntt_set_debug_checks(1 if on else 0)
 
 
 def rescale(plan: Plan, out, x, mode: int = 0, limb_begin: int = 0, stream=None):

@@ -202,6 +202,22 @@ __global__ __launch_bounds__(kThreads) void rescale_kernel(uint64_t* __restrict_
   }
 }
 
+// Debug input check: how many residues are >= their prime.  One count per block
+// (__syncthreads_count), added by one lane through a vector atomic.
+__global__ __launch_bounds__(kThreads) void count_noncanonical_kernel(const uint64_t* __restrict__ data,
+                                                                      const ModInfo* __restrict__ mods,
+                                                                      uint32_t logn, uint32_t num_limbs,
+                                                                      uint32_t limb_begin, uint64_t total,
+                                                                      unsigned long long* __restrict__ count) {
+  const uint64_t idx = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+  int bad = 0;
+  if (idx < total) bad = data[idx] >= mods[limb_begin + (uint32_t)((idx >> logn) % num_limbs)].q;
+  const int c = __syncthreads_count(bad);
+  if (threadIdx.x == 0 && c) atomicAdd(count, (unsigned long long)c);
+}
+
+__global__ void zero_counter_kernel(unsigned long long* count) { *count = 0; }
+
 uint32_t blocks_for(uint64_t work) { return (uint32_t)((work + kThreads - 1) / kThreads); }
 
 }  // namespace
@@ -245,6 +261,20 @@ hipError_t launch_automorph(const ntt_plan* p, uint64_t* out, const uint64_t* in
     hipLaunchKernelGGL(automorph_ntt_kernel, dim3(blocks_for(total)), dim3(kThreads), 0, s, out, in, p->logn,
                        (uint32_t)(g % two_n), total);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_count_noncanonical(const ntt_plan* p, const uint64_t* data, uint64_t rows, uint32_t limb_begin,
+                                     uint32_t num_limbs, unsigned long long* count, hipStream_t s) {
+  const uint64_t total = rows * num_limbs * p->n;
+  if (!total) return hipSuccess;
+  hipLaunchKernelGGL(count_noncanonical_kernel, dim3(blocks_for(total)), dim3(kThreads), 0, s, data, p->d_mods,
+                     p->logn, num_limbs, limb_begin, total, count);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_counter(unsigned long long* count, hipStream_t s) {
+  hipLaunchKernelGGL(zero_counter_kernel, dim3(1), dim3(1), 0, s, count);
   return hipGetLastError();
 }
 

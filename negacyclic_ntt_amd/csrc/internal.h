@@ -52,6 +52,7 @@ struct ntt_plan {
   nntt::Narrow::Tw* d_inv32 = nullptr;
   nntt::ModInfo* d_mods = nullptr;    // [L]
   nntt::RescaleC* d_rescale = nullptr;  // triangle over the plan's primes, L (L - 1) / 2 entries
+  unsigned long long* d_check = nullptr;  // one counter for the debug input checks
 };
 
 namespace nntt {
@@ -94,6 +95,15 @@ hipError_t launch_tensor(const ntt_plan* p, uint64_t* out, const uint64_t* a, co
                          uint32_t limb_begin, uint32_t num_limbs, hipStream_t s);
 hipError_t launch_automorph(const ntt_plan* p, uint64_t* out, const uint64_t* in, uint64_t g, int domain,
                             uint64_t batch, uint32_t limb_begin, uint32_t num_limbs, hipStream_t s);
+// Adds the number of residues >= their prime in data [rows][num_limbs][n] to *count.
+hipError_t launch_count_noncanonical(const ntt_plan* p, const uint64_t* data, uint64_t rows, uint32_t limb_begin,
+                                     uint32_t num_limbs, unsigned long long* count, hipStream_t s);
+hipError_t launch_zero_counter(unsigned long long* count, hipStream_t s);
+// Debug input checks (capi.cpp): when enabled, counts the non-canonical residues of an
+// input [rows][num_limbs][n] and waits for the result: NTT_EINVAL if any, else NTT_OK.
+// Disabled: NTT_OK without touching the device.
+int debug_check_inputs(const ntt_plan* p, const uint64_t* data, uint64_t rows, uint32_t limb_begin,
+                       uint32_t num_limbs, hipStream_t s);
 // in: [batch][num_limbs][n] over primes [limb_begin, limb_begin + num_limbs); out: [batch][num_limbs - 1][n].
 hipError_t launch_rescale(const ntt_plan* p, uint64_t* out, const uint64_t* in, uint64_t batch, uint32_t limb_begin,
                           uint32_t num_limbs, bool nearest, hipStream_t s);

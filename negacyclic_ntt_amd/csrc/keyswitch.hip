@@ -679,6 +679,14 @@ struct KsIo {
   const uint64_t* in;
 };
 
+// Debug input checks of a key-switch call: rows of the input over Q, rows of the key over Q u P.
+int ks_debug_inputs(const ntt_ks_plan* p, const uint64_t* in, uint64_t in_rows, const uint64_t* key,
+                    uint64_t key_rows, hipStream_t s) {
+  int rc = debug_check_inputs(p->qp, in, in_rows, 0, p->nq, s);
+  if (rc == NTT_OK) rc = debug_check_inputs(p->qp, key, key_rows, 0, p->nq + p->np, s);
+  return rc;
+}
+
 // Validation shared by the entry points; returns NTT_OK or the error.
 int ks_check(const ntt_ks_plan* p, uint64_t* out, const KsIo& io, const uint64_t* ksk, uint64_t batch,
              void* workspace, size_t workspace_bytes) {
@@ -818,8 +826,9 @@ extern "C" int keyswitch(const ntt_ks_plan* p, uint64_t* out, const uint64_t* ct
   if (!(galois_elt & 1) || galois_elt >= 2ull * n) return NTT_EINVAL;
   if (batch == 0) return NTT_OK;
   const KsIo io{ct ? ct + plane : nullptr, 2 * plane, ct, 2 * plane, 1u, batch * 2 * plane * 8, ct};
-  const int rc = ks_check(p, out, io, ksk, batch, workspace, workspace_bytes);
+  int rc = ks_check(p, out, io, ksk, batch, workspace, workspace_bytes);
   if (rc) return rc;
+  if ((rc = ks_debug_inputs(p, ct, 2 * batch, ksk, p->dnum * 2, (hipStream_t)stream))) return rc;
   return ks_run(p, out, io, ksk, galois_elt, batch, workspace, (hipStream_t)stream);
 }
 
@@ -830,8 +839,9 @@ extern "C" int relinearize(const ntt_ks_plan* p, uint64_t* out, const uint64_t* 
   if (batch == 0) return NTT_OK;
   // decompose d2, add (d0, d1); no automorphism (g = 1)
   const KsIo io{d ? d + 2 * plane : nullptr, 3 * plane, d, 3 * plane, 3u, batch * 3 * plane * 8, d};
-  const int rc = ks_check(p, out, io, rlk, batch, workspace, workspace_bytes);
+  int rc = ks_check(p, out, io, rlk, batch, workspace, workspace_bytes);
   if (rc) return rc;
+  if ((rc = ks_debug_inputs(p, d, 3 * batch, rlk, p->dnum * 2, (hipStream_t)stream))) return rc;
   return ks_run(p, out, io, rlk, 1, batch, workspace, (hipStream_t)stream);
 }
 
@@ -868,6 +878,8 @@ extern "C" int keyswitch_hoisted(const ntt_ks_plan* p, uint64_t* out, const uint
       ranges_overlap(workspace, need, ksk, ksk_bytes))
     return NTT_EOVERLAP;
 
+  int rc = ks_debug_inputs(p, ct, 2 * batch, ksk, (uint64_t)num_rot * dnum * 2, (hipStream_t)stream);
+  if (rc) return rc;
   DeviceGuard g(qp->device);
   if (!g.ok) return NTT_EDEVICE;
   hipStream_t s = (hipStream_t)stream;
@@ -879,7 +891,7 @@ extern "C" int keyswitch_hoisted(const ntt_ks_plan* p, uint64_t* out, const uint
   uint64_t* ext = (uint64_t*)workspace;
   uint64_t* acc = ext + batch * (uint64_t)dnum * qplane;
   const KsIo io{ct + plane, 2 * plane, ct, 2 * plane, 1u, ct_bytes, ct};
-  int rc = ks_modup(p, ext, io, 1, batch, s);  // no automorphism: the digits are shared
+  rc = ks_modup(p, ext, io, 1, batch, s);  // no automorphism: the digits are shared
   if (rc) return rc;
   if (launch_ntt(qp, ext, batch * dnum, 0, nqp, false, s) != hipSuccess) return NTT_EDEVICE;
   const uint32_t seglog = std::min(qp->logn, 9u);
@@ -969,6 +981,8 @@ extern "C" int modraise(const ntt_mr_plan* p, uint64_t* out, const uint64_t* in,
   if (batch == 0) return NTT_OK;
   if (!out || !in || (((uintptr_t)out | (uintptr_t)in) & 15u)) return NTT_EINVAL;
   if (ranges_overlap(out, batch * p->to * n * 8, in, batch * p->from * n * 8)) return NTT_EOVERLAP;
+  const int rc = debug_check_inputs(plan, in, batch, 0, p->from, (hipStream_t)stream);
+  if (rc) return rc;
   DeviceGuard g(plan->device);
   if (!g.ok) return NTT_EDEVICE;
   hipStream_t s = (hipStream_t)stream;

@@ -152,11 +152,13 @@ static void free_device(ntt_plan* p) {
   (void)hipFree(p->d_inv32);
   (void)hipFree(p->d_mods);
   (void)hipFree(p->d_rescale);
+  (void)hipFree(p->d_check);
   p->d_fwd = p->d_inv = nullptr;
   p->d_fwd60 = p->d_inv60 = nullptr;
   p->d_fwd32 = p->d_inv32 = nullptr;
   p->d_mods = nullptr;
   p->d_rescale = nullptr;
+  p->d_check = nullptr;
 }
 
 // Rescale constants for every pair l < k.  The inverses of q_k mod q_l for all k > l
@@ -299,6 +301,10 @@ extern "C" int ntt_plan_create(ntt_plan** out, uint32_t n, const uint64_t* prime
     if (rc == NTT_OK) rc = upload(&p->d_fwd32, fwd32.data(), tn * sizeof(Narrow::Tw));
     if (rc == NTT_OK) rc = upload(&p->d_inv32, inv32.data(), tn * sizeof(Narrow::Tw));
     if (rc == NTT_OK) rc = upload(&p->d_mods, p->h_mods.data(), num_primes * sizeof(ModInfo));
+    if (rc == NTT_OK) {
+      const unsigned long long zero = 0;
+      rc = upload(&p->d_check, &zero, sizeof(zero));
+    }
     if (rc == NTT_OK && num_primes > 1) {
       std::vector<RescaleC> tri;
       rc = rescale_triangle(primes, num_primes, &tri);

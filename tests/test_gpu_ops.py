@@ -184,3 +184,52 @@ def test_device_validation(B):
         B.ntt_forward(plan, t[:, :, :1024])
     with pytest.raises(ValueError):
         B.ntt_forward(plan, t.transpose(0, 1))
+
+
+def test_count_noncanonical_and_debug_checks():
+    """The input check counts exactly the planted residues >= q (q itself, q + 5, 2^63 - 1);
+    with debug checks on, entry points reject such inputs before launching and leave
+    their outputs untouched; with checks off they run (result unspecified)."""
+    require_gpu()
+    import ctypes
+    import torch
+    from negacyclic_ntt_amd import binding as B
+    n = 1 << 12
+    ps = list(primes(60, 2 * n, 4))
+    plan = B.Plan(n, ps, 0)
+    x = residues((2, 4, n), ps, 9100)
+    assert B.count_noncanonical(plan, dev(x)) == 0
+    bad = x.copy()
+    bad[0, 1, 7] = ps[1]
+    bad[1, 3, 0] = ps[3] + 5
+    bad[1, 0, n - 1] = (1 << 63) - 1
+    tb = dev(bad)
+    announce("count noncanonical")
+    assert B.count_noncanonical(plan, tb) == 3
+    assert B.count_noncanonical(plan, tb[:, 1:3].contiguous(), limb_begin=1) == 1
+    L = B.lib()
+    V = ctypes.c_void_p
+    B.set_debug_checks(True)
+    try:
+        before = host(tb).copy()
+        assert L.ntt_forward(plan.handle, V(tb.data_ptr()), 2, 0, 4, None) == B.NTT_EINVAL
+        assert np.array_equal(host(tb), before)  # nothing ran
+        good = dev(x)
+        assert L.ntt_forward(plan.handle, V(good.data_ptr()), 2, 0, 4, None) == B.NTT_OK
+        out = torch.zeros_like(good)
+        assert L.poly_mul_ntt(plan.handle, V(out.data_ptr()), V(good.data_ptr()), V(tb.data_ptr()), 2, 0, 4,
+                              None) == B.NTT_EINVAL
+        assert not host(out).any()
+        # key-switch: a non-canonical key is rejected
+        ks_primes = list(primes(60, 1 << 17, 8))
+        kplan = B.Plan(n, ks_primes, 0)
+        ks = B.KeySwitchPlan(kplan, 6, 2, 3)
+        ct = dev(residues((1, 2, 6, n), ks_primes[:6], 9101))
+        key = residues((3, 2, 8, n), ks_primes, 9102)
+        key[2, 1, 7, 5] = ks_primes[7]
+        with pytest.raises(B.NttError):
+            B.keyswitch(ks, torch.zeros_like(ct), ct, dev(key), 5)
+    finally:
+        B.set_debug_checks(False)
+    assert L.ntt_forward(plan.handle, V(tb.data_ptr()), 2, 0, 4, None) == B.NTT_OK  # checks off: it runs
+    torch.cuda.synchronize()
