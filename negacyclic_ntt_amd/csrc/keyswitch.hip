@@ -357,6 +357,10 @@ __global__ __launch_bounds__(kKsThreads) void mac_hoisted_kernel(uint64_t* __res
   __syncthreads();
   if (!active) return;
   const uint64_t q = mods[t].q, ninv = mods[t].mont_ninv;
+#ifndef NNTT_HOIST_UNROLL
+#define NNTT_HOIST_UNROLL 2
+#endif
+#pragma unroll NNTT_HOIST_UNROLL
   for (uint32_t r = 0; r < R; ++r) {
     const uint32_t g = ha.g[r];
     const uint32_t k0 = (ntt_slot(s0, ha.h[r], logn) & ~(seg - 1)) + i2;
@@ -418,31 +422,48 @@ __global__ __launch_bounds__(kKsThreads) void moddown_kernel(uint64_t* __restric
     if (i >= (int)np_) break;
     y[i] = a[(uint64_t)(nq + i) * n];
   }
-  constexpr int S = kMaxSpecial;
-  uint32_t vl[KP], vh[KP];
-  if constexpr (B60)
-    garner30<KP, S>(y, v, vl, vh, np_, kc.moduli + nq, kc.ninv + nq, kc.p_garner, kc.p_garner30);
-  else
-    garner<B60, KP, S>(y, v, np_, kc.moduli + nq, kc.p_garner);
   const bool adds = (add_mask >> comp) & 1u;
   const uint64_t* c0 = add + (uint64_t)b * add_stride + (uint64_t)comp * nq * n;
   const Gather gi = gather_index(e, h, logn);
   uint64_t* o = out + (uint64_t)bc * nq * n + e;
   const uint32_t per = (nq + groups - 1) / groups;
   const uint32_t l0 = grp * per, l1 = min(nq, l0 + per);
-#pragma unroll 4
-  for (uint32_t l = l0; l < l1; ++l) {
-    const uint64_t q = kc.moduli[l];
-    uint64_t r;  // (X mod P) mod q_l
-    if constexpr (B60) r = dot30<KP>(vl, vh, np_, kc.p_eval30 + (size_t)l * S, q, kc.ninv[l]);
-    else r = mixed_radix_eval<B60, KP>(v, np_, kc.p_eval + (size_t)l * S, q);
-    const uint64_t d = sub_mod(a[(uint64_t)l * n], r, q);
-    uint64_t res = csub(shoup<B60>(d, kc.p_inv[l], q), q);
-    if (adds) {
-      const uint64_t s = c0[(uint64_t)l * n + gi.src];
-      res = add_mod(res, gi.neg ? neg_mod(s, q) : s, q);
+  // The output limbs go in chunks whose loads (accumulator residue, gathered addend)
+  // are all issued together; the first chunk's before the Garner digits are computed.
+  constexpr int CH = 8;
+  uint64_t av[CH], cv[CH];
+  auto prefetch = [&](uint32_t lb) {
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const uint32_t l = lb + k;
+      if (l < l1) {
+        av[k] = a[(uint64_t)l * n];
+        cv[k] = adds ? c0[(uint64_t)l * n + gi.src] : 0;
+      }
     }
-    o[(uint64_t)l * n] = res;
+  };
+  prefetch(l0);
+  constexpr int S = kMaxSpecial;
+  uint32_t vl[KP], vh[KP];
+  if constexpr (B60)
+    garner30<KP, S>(y, v, vl, vh, np_, kc.moduli + nq, kc.ninv + nq, kc.p_garner, kc.p_garner30);
+  else
+    garner<B60, KP, S>(y, v, np_, kc.moduli + nq, kc.p_garner);
+  for (uint32_t lb = l0; lb < l1; lb += CH) {
+    if (lb != l0) prefetch(lb);
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const uint32_t l = lb + k;
+      if (l >= l1) break;
+      const uint64_t q = kc.moduli[l];
+      uint64_t r;  // (X mod P) mod q_l
+      if constexpr (B60) r = dot30<KP>(vl, vh, np_, kc.p_eval30 + (size_t)l * S, q, kc.ninv[l]);
+      else r = mixed_radix_eval<B60, KP>(v, np_, kc.p_eval + (size_t)l * S, q);
+      const uint64_t d = sub_mod(av[k], r, q);
+      uint64_t res = csub(shoup<B60>(d, kc.p_inv[l], q), q);
+      if (adds) res = add_mod(res, gi.neg ? neg_mod(cv[k], q) : cv[k], q);
+      o[(uint64_t)l * n] = res;
+    }
   }
 }
 
