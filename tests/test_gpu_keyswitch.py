@@ -155,3 +155,53 @@ def test_keyswitch_validation(B):
     assert L.keyswitch_plan_create(ctypes.byref(h), plan.handle, 24, 8, 5) == B.NTT_EINVAL  # 24 % 5
     assert L.keyswitch_plan_create(ctypes.byref(h), plan.handle, 24, 9, 3) == B.NTT_EINVAL  # beyond the plan
     assert L.keyswitch_plan_create(ctypes.byref(h), plan.handle, 24, 8, 1) == B.NTT_EUNSUPPORTED  # alpha 24
+
+
+def test_graph_capture_replays_match_eager(B):
+    """The entry points allocate nothing and launch on the caller's stream, so a HIP
+    graph can hold them.  Capture: forward NTT (out of place, g = 1), pointwise
+    product, inverse NTT, rotation key-switch; replay three times with eager work in
+    between and compare every replay with the eager results."""
+    import torch
+    n = 1 << 12
+    qp, plan, ks = _setup(B, n)
+    x = dev(residues((2, 24, n), qp[:24], 9950))
+    bb = dev(residues((2, 24, n), qp[:24], 9951))
+    ct = dev(residues((1, 2, 24, n), qp[:24], 9952))
+    ksk = dev(residues((3, 2, 32, n), qp, 9953))
+    ws = B.workspace(ks, 1)
+    f = torch.empty_like(x)
+    c = torch.empty_like(x)
+    ko = torch.empty_like(ct)
+
+    def body():
+        B.ntt_forward_galois(plan, f, x, 1)
+        B.poly_mul_ntt(plan, c, f, bb)
+        B.ntt_inverse(plan, c)
+        B.keyswitch(ks, ko, ct, ksk, 25, ws)
+
+    announce("graph capture eager")
+    body()
+    want_c, want_k = host(c).copy(), host(ko).copy()
+    assert_bits_equal(want_c, orc.batch_ntt(orc.batch_pointwise(orc.batch_ntt(host(x), qp[:24]), host(bb), qp[:24]),
+                                            qp[:24], inverse=True), "eager pipeline vs oracle")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        body()  # warm-up on the side stream before capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    announce("graph capture")
+    with torch.cuda.graph(g):
+        body()
+    for rep in range(3):
+        c.zero_()
+        ko.zero_()
+        torch.cuda.synchronize()
+        announce("graph replay", rep)
+        g.replay()
+        torch.cuda.synchronize()
+        assert_bits_equal(host(c), want_c, f"replay {rep} pipeline")
+        assert_bits_equal(host(ko), want_k, f"replay {rep} keyswitch")
+        B.ntt_forward(plan, dev(residues((2, 24, n), qp[:24], 9960 + rep)))  # eager work between replays
