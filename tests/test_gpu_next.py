@@ -333,3 +333,38 @@ def test_modraise_validation(B):
     assert L.modraise(mr.handle, V(out.data_ptr()), V(out.data_ptr()), 2, None) == B.NTT_EOVERLAP
     assert L.modraise(mr.handle, V(out.data_ptr() + 8), V(x.data_ptr()), 2, None) == B.NTT_EINVAL
     assert L.modraise(mr.handle, V(out.data_ptr()), V(x.data_ptr()), 0, None) == B.NTT_OK
+
+
+# ---- launches larger than one grid dimension ------------------------------------------------
+
+def test_keyswitch_batch_beyond_grid_y(B):
+    """batch x digits = 4096 x 16 = 65536 exceeds the grid's y range: ModUp runs in
+    chunks (n = 8, 16 one-prime digits, 2 special primes)."""
+    n = 8
+    qp = list(primes(60, 1 << 17, 18))
+    plan = B.Plan(n, qp, 0)
+    ks = B.KeySwitchPlan(plan, 16, 2, 16)
+    ct = residues((4096, 2, 16, n), qp[:16], 9400)
+    ksk = residues((16, 2, 18, n), qp, 9401)
+    announce("keyswitch batch 4096 x dnum 16")
+    out = host(B.keyswitch(ks, dev(np.zeros_like(ct)), dev(ct), dev(ksk), 3))
+    # ciphertexts are independent: compare both ends, across the chunk boundary (4095 per chunk)
+    pick = np.r_[0:32, 4064:4096]
+    want = orc.keyswitch(np.ascontiguousarray(ct[pick]), ksk, 3, qp, 16, 16)
+    assert_bits_equal(np.ascontiguousarray(out[pick]), want, "keyswitch grid-y chunks")
+
+
+def test_rescale_and_modraise_batch_beyond_grid_y(B):
+    """70000 polynomials (n = 2): the batch is split across launches."""
+    n = 2
+    ps = list(primes(60, 2 * n, 3))
+    plan = B.Plan(n, ps, 0)
+    x = residues((70000, 3, n), ps, 9410)
+    announce("rescale batch 70000")
+    got = host(B.rescale(plan, dev(np.zeros((70000, 2, n), np.uint64)), dev(x), 1))
+    assert_bits_equal(got, orc.rescale(x, ps, 1), "rescale grid-y chunks")
+    mr = B.ModRaisePlan(plan, 1, 3)
+    lo = residues((70000, 1, n), ps[:1], 9411)
+    announce("modraise batch 70000")
+    up = host(B.modraise(mr, dev(np.zeros((70000, 3, n), np.uint64)), dev(lo)))
+    assert_bits_equal(up, orc.modraise(lo, ps, 1), "modraise grid-y chunks")
