@@ -31,6 +31,24 @@ struct RescaleC {
 __host__ __device__ inline size_t rescale_index(uint32_t k, uint32_t l) { return (size_t)k * (k - 1) / 2 + l; }
 
 constexpr uint32_t kMaxLogN = 16;
+
+// The NTT-domain automorphism in bit-reversed slot order: out[k] = in[slot(k)] with
+// 2 brv(slot) + 1 = (2 brv(k) + 1) g mod 2n, i.e. brv(slot) = g brv(k) + (g - 1) / 2
+// mod n.  It maps every aligned segment of 2^m slots onto an aligned segment: the
+// low log n - m bits of g brv(k) + c depend only on those of brv(k), which are the
+// reversed high bits of k, fixed inside the segment.
+__device__ __forceinline__ uint32_t ntt_slot(uint32_t k, uint32_t g, uint32_t logn) {
+  const uint32_t K = __brev(k) >> (32 - logn);
+  const uint32_t P = (uint32_t)(((uint64_t)K * g + (g >> 1)) & ((1u << logn) - 1));
+  return __brev(P) >> (32 - logn);
+}
+
+// Galois elements of a hoisted key-switch (and their inverses mod 2n), passed by value.
+constexpr uint32_t kMaxHoisted = 64;
+struct HoistArgs {
+  uint32_t g[kMaxHoisted];
+  uint32_t h[kMaxHoisted];
+};
 constexpr uint32_t kMaxPrimes = 4096;
 
 }  // namespace nntt
@@ -83,6 +101,11 @@ hipError_t launch_ntt_galois(const ntt_plan* p, uint64_t* out, const uint64_t* i
 bool intt_mac_supported(const ntt_plan* p);
 hipError_t launch_intt_mac(const ntt_plan* p, uint64_t* acc, const uint64_t* ext, const uint64_t* ksk, uint64_t batch,
                            uint32_t nqp, uint32_t dnum, uint32_t chunk, hipStream_t s);
+// The same for hoisted rotations: acc [num_rot][batch][2][nqp][n] from the shared digits
+// gathered through each rotation's slot permutation, keys [num_rot][dnum][2][nqp][n].
+hipError_t launch_intt_mac_hoisted(const ntt_plan* p, uint64_t* acc, const uint64_t* ext, const uint64_t* ksk,
+                                   uint64_t batch, uint32_t num_rot, uint32_t nqp, uint32_t dnum, uint32_t chunk,
+                                   const HoistArgs& ha, hipStream_t s);
 // True when every prime in [limb_begin, limb_begin + num_limbs) is below 2^30.
 bool range_is_narrow(const ntt_plan* p, uint32_t limb_begin, uint32_t num_limbs);
 // True when every prime in the range is below 2^60.

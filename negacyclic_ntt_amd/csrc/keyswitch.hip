@@ -308,23 +308,6 @@ __global__ __launch_bounds__(kKsThreads) void mac_kernel(uint64_t* __restrict__ 
 }
 
 // ---- key inner product for hoisted rotations -------------------------------------------
-// The NTT-domain automorphism in bit-reversed slot order: out[k] = in[slot(k)] with
-// 2 brv(slot) + 1 = (2 brv(k) + 1) g mod 2n, i.e. brv(slot) = g brv(k) + (g - 1) / 2
-// mod n.  It maps every aligned segment of 2^m slots onto an aligned segment: the
-// low log n - m bits of g brv(k) + c depend only on those of brv(k), which are the
-// reversed high bits of k, fixed inside the segment.
-__device__ __forceinline__ uint32_t ntt_slot(uint32_t k, uint32_t g, uint32_t logn) {
-  const uint32_t K = __brev(k) >> (32 - logn);
-  const uint32_t P = (uint32_t)(((uint64_t)K * g + (g >> 1)) & ((1u << logn) - 1));
-  return __brev(P) >> (32 - logn);
-}
-
-constexpr uint32_t kMaxHoisted = 64;
-struct HoistArgs {
-  uint32_t g[kMaxHoisted];  // Galois elements
-  uint32_t h[kMaxHoisted];  // their inverses mod 2n
-};
-
 // One block owns an aligned segment S of one limb of the NTT-domain digits and stages
 // it in LDS for all dnum digits; for rotation r it then produces the output segment
 // slot_r^-1(S) = slot_{h_r}(S), reading the key and writing the accumulators with
@@ -915,6 +898,11 @@ extern "C" int keyswitch_hoisted(const ntt_ks_plan* p, uint64_t* out, const uint
   rc = ks_modup(p, ext, io, 1, batch, s);  // no automorphism: the digits are shared
   if (rc) return rc;
   if (launch_ntt(qp, ext, batch * dnum, 0, nqp, false, s) != hipSuccess) return NTT_EDEVICE;
+  if (intt_mac_supported(qp)) {  // key products fused into the inverse transform's first pass
+    if (launch_intt_mac_hoisted(qp, acc, ext, ksk, batch, num_rot, nqp, dnum, p->mac_chunk, ha, s) != hipSuccess)
+      return NTT_EDEVICE;
+    return ks_moddown(p, out, acc, io, ha, num_rot, batch, s);
+  }
   const uint32_t seglog = std::min(qp->logn, 9u);
   const dim3 grid((nqp << (qp->logn - seglog)), (uint32_t)batch);
   hipLaunchKernelGGL(mac_hoisted_kernel, grid, dim3(kKsThreads), (size_t)dnum * (8u << seglog), s, acc, ext, ksk,

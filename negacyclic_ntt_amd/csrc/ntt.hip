@@ -618,6 +618,101 @@ __global__ __launch_bounds__(RowCfg<LOGN2>::NT) void ntt_row_mac_kernel(uint64_t
   }
 }
 
+// Hoisted rotations: accumulator row poly * nqp + t, poly = (r * batch + b) * 2 + c, is
+//   sum_j ext[b][j][t][slot_{g_r}(k)] * ksk[r][j][c][t][k]   (mod q_t)
+// for each slot k of the row tile.  A row tile is an aligned segment of slots, so the
+// slots it gathers form one aligned segment of each digit (see ntt_slot).
+template <class A, int LOGN1, int LOGN2, int DN>
+__global__ __launch_bounds__(RowCfg<LOGN2>::NT) void ntt_row_mac_hoisted_kernel(
+    uint64_t* __restrict__ acc, MacSrc ms, const void* __restrict__ tw_all, const ModInfo* __restrict__ mods,
+    uint32_t nqp, uint64_t polys, uint32_t batch, HoistArgs ha) {
+  using T = typename A::T;
+  constexpr int N1 = 1 << LOGN1, N2 = 1 << LOGN2, N = N1 * N2;
+  constexpr int NT = RowCfg<LOGN2>::NT;
+  constexpr int STRIDE = sub_stride<A>(LOGN2);
+  constexpr int BLOCKS_PER_LIMB = N1 / kRows;
+  __shared__ T lds[kRows * STRIDE];
+  const int tid = threadIdx.x;
+  const Place pl = place_block(BLOCKS_PER_LIMB, polys, nqp, 0);
+  const uint64_t row = pl.row, poly = row / nqp, rb = poly >> 1;
+  const uint32_t t = pl.limb, rot = (uint32_t)(rb / batch), g = ha.g[rot];
+  const uint64_t b = rb % batch;
+  const size_t off = (size_t)pl.tile * kRows * N2;
+  const uint64_t plane = (uint64_t)nqp * N;
+  const uint64_t* xe = ms.ext + (b * ms.dnum * nqp + t) * (uint64_t)N;
+  const uint64_t* kk = ms.ksk + (((uint64_t)rot * ms.dnum * 2 + (poly & 1)) * nqp + t) * (uint64_t)N + off;
+  const ModInfo& m = mods[t];
+  const uint64_t q = m.q, ninv = m.mont_ninv;
+
+  constexpr int kIters = (kRows * N2) / (2 * NT);
+  static_assert((kRows * N2) % (2 * NT) == 0, "whole iterations");
+#pragma unroll 2
+  for (int it = 0; it < kIters; ++it) {
+    const int e = 2 * tid + it * 2 * NT;
+    const uint32_t k0 = (uint32_t)(off + e);
+    const uint32_t s0 = ntt_slot(k0, g, LOGN1 + LOGN2), s1 = ntt_slot(k0 + 1, g, LOGN1 + LOGN2);
+    Acc128 a0{0, 0}, a1{0, 0};
+    uint64_t r0 = 0, r1 = 0;
+    if constexpr (DN > 0) {
+      uint64_t d0[DN], d1[DN];
+      ulonglong2 k[DN];
+#pragma unroll
+      for (int j = 0; j < DN; ++j) {
+        d0[j] = xe[j * plane + s0];
+        d1[j] = xe[j * plane + s1];
+        k[j] = *reinterpret_cast<const ulonglong2*>(kk + 2 * j * plane + e);
+      }
+#pragma unroll
+      for (int j = 0; j < DN; ++j) {
+        mac128(a0, d0[j], k[j].x);
+        mac128(a1, d1[j], k[j].y);
+      }
+      r0 = csub(redc(a0, q, ninv), q);
+      r1 = csub(redc(a1, q, ninv), q);
+    } else {
+      uint32_t c = 0;
+      for (uint32_t j = 0; j < ms.dnum; ++j) {
+        const ulonglong2 k = *reinterpret_cast<const ulonglong2*>(kk + 2 * j * plane + e);
+        mac128(a0, xe[j * plane + s0], k.x);
+        mac128(a1, xe[j * plane + s1], k.y);
+        if (++c == ms.chunk || j + 1 == ms.dnum) {
+          r0 = add_mod(r0, csub(redc(a0, q, ninv), q), q);
+          r1 = add_mod(r1, csub(redc(a1, q, ninv), q), q);
+          a0 = Acc128{0, 0};
+          a1 = Acc128{0, 0};
+          c = 0;
+        }
+      }
+    }
+    const int sub = e / N2, pos = e % N2;
+    lds[sub * STRIDE + lpos<A>(pos)] = (T)r0;
+    lds[sub * STRIDE + lpos<A>(pos + 1)] = (T)r1;
+  }
+  __syncthreads();
+
+  const typename A::Tw* tw = table_of<A>(tw_all, t, N);
+  const T qt = modulus<A>(m);
+  auto get_sub = [&](int sub) {
+    SubParams<A> sp;
+    sp.tw = tw;
+    sp.q = qt;
+    sp.prefix = (uint32_t)N1 + (uint32_t)(pl.tile * kRows + sub);
+    return sp;
+  };
+  run_passes<A, false, LOGN2, kRows, NT, 0>(lds, tid, get_sub);
+
+  uint64_t* base = acc + row * N + off;
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
+    const int e = 2 * tid + it * 2 * NT;
+    const int sub = e / N2, pos = e % N2;
+    ulonglong2 v;
+    v.x = A::widen(lds[sub * STRIDE + lpos<A>(pos)]);
+    v.y = A::widen(lds[sub * STRIDE + lpos<A>(pos + 1)]);
+    *reinterpret_cast<ulonglong2*>(base + e) = v;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // What one launch sequence computes.
 enum class Op { kForward, kInverse, kForwardGalois };
@@ -696,6 +791,36 @@ hipError_t launch_mac_split(const ntt_plan* p, uint64_t* acc, const MacSrc& ms, 
   hipLaunchKernelGGL((ntt_col_kernel<A, LOGN1, LOGN2, false, true, false>), col_grid, col_block, 0, s, acc, acc, tw,
                      p->d_mods, nqp, 0u, polys, 1u);
   return hipGetLastError();
+}
+
+template <class A, int LOGN1, int LOGN2>
+hipError_t launch_mac_hoisted_split(const ntt_plan* p, uint64_t* acc, const MacSrc& ms, uint64_t batch,
+                                    uint32_t num_rot, uint32_t nqp, const HoistArgs& ha, hipStream_t s) {
+  const void* tw = tables_for<A>(p, Op::kInverse);
+  const uint64_t polys = 2 * batch * num_rot, rows = polys * nqp;
+  const dim3 col_grid((uint32_t)(rows * ((1u << LOGN2) / kCols))), col_block(ColCfg<LOGN1>::NT);
+  const dim3 row_grid((uint32_t)(rows * ((1u << LOGN1) / kRows))), row_block(RowCfg<LOGN2>::NT);
+  const bool one = ms.dnum <= ms.chunk;
+#define NNTT_MAC_ROW(D)                                                                                      \
+  hipLaunchKernelGGL((ntt_row_mac_hoisted_kernel<A, LOGN1, LOGN2, D>), row_grid, row_block, 0, s, acc, ms, tw, \
+                     p->d_mods, nqp, polys, (uint32_t)batch, ha)
+  if (one && ms.dnum == 1) NNTT_MAC_ROW(1);
+  else if (one && ms.dnum == 2) NNTT_MAC_ROW(2);
+  else if (one && ms.dnum == 3) NNTT_MAC_ROW(3);
+  else if (one && ms.dnum == 4) NNTT_MAC_ROW(4);
+  else NNTT_MAC_ROW(0);
+#undef NNTT_MAC_ROW
+  hipLaunchKernelGGL((ntt_col_kernel<A, LOGN1, LOGN2, false, true, false>), col_grid, col_block, 0, s, acc, acc, tw,
+                     p->d_mods, nqp, 0u, polys, 1u);
+  return hipGetLastError();
+}
+
+template <class A>
+hipError_t launch_mac_hoisted_any(const ntt_plan* p, uint64_t* acc, const MacSrc& ms, uint64_t batch,
+                                  uint32_t num_rot, uint32_t nqp, const HoistArgs& ha, hipStream_t s) {
+  if (p->logn == 15) return launch_mac_hoisted_split<A, 7, 8>(p, acc, ms, batch, num_rot, nqp, ha, s);
+  if (p->logn == 16) return launch_mac_hoisted_split<A, 8, 8>(p, acc, ms, batch, num_rot, nqp, ha, s);
+  return hipErrorNotSupported;
 }
 
 template <class A>
@@ -777,6 +902,17 @@ hipError_t launch_intt_mac(const ntt_plan* p, uint64_t* acc, const uint64_t* ext
   if (range_is_narrow(p, 0, nqp)) return launch_mac_any<Narrow>(p, acc, ms, batch, nqp, s);
   if (range_below60(p, 0, nqp)) return launch_mac_any<Wide60>(p, acc, ms, batch, nqp, s);
   return launch_mac_any<Wide>(p, acc, ms, batch, nqp, s);
+}
+
+hipError_t launch_intt_mac_hoisted(const ntt_plan* p, uint64_t* acc, const uint64_t* ext, const uint64_t* ksk,
+                                   uint64_t batch, uint32_t num_rot, uint32_t nqp, uint32_t dnum, uint32_t chunk,
+                                   const HoistArgs& ha, hipStream_t s) {
+  if (!intt_mac_supported(p)) return hipErrorNotSupported;
+  if (batch == 0) return hipSuccess;
+  const MacSrc ms{ext, ksk, dnum, chunk};
+  if (range_is_narrow(p, 0, nqp)) return launch_mac_hoisted_any<Narrow>(p, acc, ms, batch, num_rot, nqp, ha, s);
+  if (range_below60(p, 0, nqp)) return launch_mac_hoisted_any<Wide60>(p, acc, ms, batch, num_rot, nqp, ha, s);
+  return launch_mac_hoisted_any<Wide>(p, acc, ms, batch, num_rot, nqp, ha, s);
 }
 
 hipError_t launch_ntt_galois(const ntt_plan* p, uint64_t* out, const uint64_t* in, uint64_t g, uint64_t batch,

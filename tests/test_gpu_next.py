@@ -245,6 +245,23 @@ def test_hoisted_shapes_vs_oracle(B, logn, nq, npr, dnum, batch):
                       orc.keyswitch_hoisted(ct, ksk, gs, qp[: nq + npr], nq, dnum), "hoisted shape")
 
 
+@pytest.mark.parametrize("bits,nq,npr,dnum", [(60, 12, 4, 3), (60, 10, 2, 5), (62, 10, 3, 5), (62, 8, 4, 2)])
+def test_hoisted_fused_product_paths(B, bits, nq, npr, dnum):
+    """n = 2^15: the rotations' key products run inside the inverse transform's first
+    pass (compile-time and runtime digit counts; 62-bit primes take several
+    reductions per product sum)."""
+    n = 1 << 15
+    qp = list(primes(bits, 2 * n, nq + npr))
+    plan = B.Plan(n, qp, 0)
+    ks = B.KeySwitchPlan(plan, nq, npr, dnum)
+    gs = [5, 2 * n - 1, 25, 1]
+    ct = residues((2, 2, nq, n), qp[:nq], 7850 + dnum + bits)
+    ksk = residues((len(gs), dnum, 2, nq + npr, n), qp, 7860 + dnum + bits)
+    announce("hoisted fused", bits, nq, npr, dnum)
+    assert_bits_equal(_hoisted_gpu(B, ks, ct, ksk, gs), orc.keyswitch_hoisted(ct, ksk, gs, qp, nq, dnum),
+                      "hoisted fused product")
+
+
 def test_hoisted_identity_equals_keyswitch(B):
     n = 1 << 12
     qp, plan, ks = _ks_setup(B, n)
