@@ -14,6 +14,9 @@ namespace nntt {
 namespace {
 
 constexpr int kThreads = 256;
+#ifndef NNTT_TENSOR_SUM_REDC
+#define NNTT_TENSOR_SUM_REDC 1
+#endif
 
 // Streaming 16-byte accesses: every residue is touched once, so loads and stores are
 // marked non-temporal (they bypass reuse-oriented cache allocation).
@@ -66,7 +69,8 @@ __global__ __launch_bounds__(kThreads) void tensor_kernel(uint64_t* __restrict__
   const uint64_t plane = (uint64_t)num_limbs << logn;  // elements per component
   const uint64_t e = 2 * p;                            // flat index in [batch][L][n]
   const uint64_t bi = e / plane, off = e % plane;
-  const Barrett br = mods[limb_begin + (uint32_t)(off >> logn)].br;
+  const ModInfo& mi = mods[limb_begin + (uint32_t)(off >> logn)];
+  const Barrett br = mi.br;
   const uint64_t q = br.q;
   const uint64_t* a0 = a + bi * 2 * plane + off;
   const uint64_t* b0 = b + bi * 2 * plane + off;
@@ -78,8 +82,23 @@ __global__ __launch_bounds__(kThreads) void tensor_kernel(uint64_t* __restrict__
   u64x2 r0, r1, r2;
   r0.x = barrett_mul(x0.x, y0.x, br);
   r0.y = barrett_mul(x0.y, y0.y, br);
+#if NNTT_TENSOR_SUM_REDC
+  // d1 = a0 b1 + a1 b0: the exact 128-bit sum (< 2 q^2 < q 2^64) reduced once by
+  // Montgomery (which divides by 2^64), then one Shoup product by 2^64 mod q.
+  {
+    const Wide::Tw r64{mi.r64, mi.r64_shoup};
+    Acc128 s0{0, 0}, s1{0, 0};
+    mac128(s0, x0.x, y1.x);
+    mac128(s0, x1.x, y0.x);
+    mac128(s1, x0.y, y1.y);
+    mac128(s1, x1.y, y0.y);
+    r1.x = csub(Wide::mul(redc(s0, q, mi.mont_ninv), r64, q), q);
+    r1.y = csub(Wide::mul(redc(s1, q, mi.mont_ninv), r64, q), q);
+  }
+#else
   r1.x = add_mod(barrett_mul(x0.x, y1.x, br), barrett_mul(x1.x, y0.x, br), q);
   r1.y = add_mod(barrett_mul(x0.y, y1.y, br), barrett_mul(x1.y, y0.y, br), q);
+#endif
   r2.x = barrett_mul(x1.x, y1.x, br);
   r2.y = barrett_mul(x1.y, y1.y, br);
   st_stream(d0, r0);

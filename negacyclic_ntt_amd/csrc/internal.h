@@ -19,6 +19,7 @@ struct ModInfo {
   uint32_t n_inv32, n_inv_shoup32;  // narrow (q < 2^30) Shoup pair, else 0
   Barrett br;
   uint64_t mont_ninv;  // -q^-1 mod 2^64 (Montgomery reduction with R = 2^64)
+  uint64_t r64, r64_shoup;  // 2^64 mod q and floor(r64 2^64 / q): undoes a Montgomery reduction
 };
 
 // Constants to divide by prime k and express the quotient modulo prime l < k (rescale).

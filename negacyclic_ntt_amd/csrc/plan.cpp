@@ -289,6 +289,8 @@ extern "C" int ntt_plan_create(ntt_plan** out, uint32_t n, const uint64_t* prime
     uint64_t inv = q;  // Newton: q * q == 1 mod 8, each step doubles the correct bits
     for (int it = 0; it < 5; ++it) inv *= 2 - q * inv;
     m.mont_ninv = 0 - inv;
+    m.r64 = (uint64_t)(((u128)1 << 64) % q);
+    m.r64_shoup = (uint64_t)(((u128)m.r64 << 64) / q);
   }
 
   if (device >= 0) {
