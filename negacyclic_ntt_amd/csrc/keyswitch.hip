@@ -11,16 +11,19 @@
 //      section 4.2) and reduced onto every prime of Q u P;
 //   3. forward NTT of every extended digit;
 //   4. key inner product acc_c = sum_j NTT(D_j) * ksk[j][c] (FHElium's key-switch
-//      multiply-accumulate);
-//   5. inverse NTT of both accumulators;
+//      multiply-accumulate) -- for n >= 2^15 computed inside the first pass of
+//   5. the inverse NTT of both accumulators (ntt.hip), else by mac_kernel;
 //   6. ModDown (exact floor, FHElium's "QP-to-Q ModDown"):
 //      out_c = floor(X_c / P) mod q_l = (acc_c[l] - (X_c mod P)) * P^-1 mod q_l,
 //      X_c mod P from the P residues by Garner; out_0 += sigma_g(c0).
 // Garner: with residues x_i modulo m_i, the mixed-radix digits are
 //   v_i = (x_i - sum_{k<i} v_k prod_{j<k} m_j) * (prod_{j<i} m_j)^-1  mod m_i,
 // and D = sum_i v_i prod_{j<i} m_j lies in [0, prod m_i); D mod p is then
-// sum_i v_i (prod_{j<i} m_j mod p).  Every product is a Shoup product by a
-// plan constant; partial sums stay in [0, 2p).
+// sum_i v_i (prod_{j<i} m_j mod p).  Below 2^60 the sums of products by plan
+// constants are 30-bit-half dot products with one Montgomery reduction (dot30);
+// otherwise each product is a Shoup product with partial sums kept in [0, 2p).
+// The extended digits are stored times 2^64 (Montgomery form) so that the key
+// product needs one Montgomery reduction per output.
 #include <string.h>
 
 #include <algorithm>
@@ -258,6 +261,7 @@ __global__ __launch_bounds__(kKsThreads) void modup_kernel(uint64_t* __restrict_
 }
 
 // ---- key inner product -----------------------------------------------------------
+// (Rings below 2^15; larger rings fuse this product into the inverse NTT, ntt.hip.)
 // acc[b][c][t][e] = sum_j ext[b][j][t][e] * ksk[j][c][t][e]  (mod q_t), two coefficients
 // per thread.  The digits carry a factor 2^64, so the exact 128-bit sum of up to
 // `chunk` products (chunk q_t <= 2^64 keeps it below q_t 2^64) is Montgomery-reduced
@@ -308,6 +312,7 @@ __global__ __launch_bounds__(kKsThreads) void mac_kernel(uint64_t* __restrict__ 
 }
 
 // ---- key inner product for hoisted rotations -------------------------------------------
+// (Rings below 2^15; larger rings fuse this product into the inverse NTT, ntt.hip.)
 // One block owns an aligned segment S of one limb of the NTT-domain digits and stages
 // it in LDS for all dnum digits; for rotation r it then produces the output segment
 // slot_r^-1(S) = slot_{h_r}(S), reading the key and writing the accumulators with
