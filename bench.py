@@ -37,12 +37,26 @@ CALIBRATION_COPY_BYTES = 256 << 20
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def kernel_sources_digest():
+def code_text(source: str) -> str:
+    """C/HIP source with comments removed and whitespace collapsed: two sources
+    with the same code text compile to the same kernels."""
+    import re
+    source = re.sub(r"/\*.*?\*/", " ", source, flags=re.S)
+    source = re.sub(r"//[^\n]*", " ", source)
+    return " ".join(source.split())
+
+
+def kernel_sources_digest(read=None):
+    """sha256/16 over the code text of modarith.h + ntt.hip (comments excluded, so a
+    comment edit does not invalidate counters taken on the same kernels)."""
     import hashlib
+    if read is None:
+        def read(name):
+            with open(os.path.join(ROOT, "negacyclic_ntt_amd", "csrc", name)) as fh:
+                return fh.read()
     h = hashlib.sha256()
     for f in ("modarith.h", "ntt.hip"):
-        with open(os.path.join(ROOT, "negacyclic_ntt_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        h.update(code_text(read(f)).encode())
     return h.hexdigest()[:16]
 
 

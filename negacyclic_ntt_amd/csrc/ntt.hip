@@ -21,6 +21,10 @@
 //                     residues fit the 160 KiB LDS of one gfx950 workgroup).
 //   ntt_col_kernel / ntt_row_kernel : the two halves for n = 2^15, 2^16; the
 //                     intermediate goes through L2/MALL/HBM between launches.
+//   ntt_row_mac_kernel / ntt_row_mac_hoisted_kernel : the inverse transform's first
+//                     (row) pass with the key-switch's key product computed as the
+//                     row tile is loaded (one rotation, or hoisted rotations whose
+//                     digits are gathered through the NTT-domain slot permutation).
 // Inside a workgroup, each thread holds one radix-2^r "set" (up to 16 residues)
 // in registers and runs r stages on it; sets are exchanged through LDS between
 // passes.  LDS rows are padded by one slot per 128 bytes so strided set accesses
