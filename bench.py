@@ -170,6 +170,15 @@ def next_rows(B, plan, ksp, ws, primes, W, KS, C, ct, ksk, galois, reps):
         out["relinearize"] = {"us": round(ms_rel * 1e3, 2), "per_s": round(1e3 / ms_rel, 1),
                               "keyswitch_us_same_run": round(ms_ks * 1e3, 2)}
         del d, rel
+        # the same rotation on 4 ciphertexts in one call: larger launches fill the GPU
+        nb = 4
+        ctb = ct.repeat(nb, 1, 1, 1).contiguous()
+        outb = torch.empty_like(ctb)
+        wsb = B.workspace(ksp, nb)
+        ms_b = time_op(lambda: B.keyswitch(ksp, outb, ctb, ksk, galois[0], wsb), reps)
+        out["keyswitch_batch4"] = {"us": round(ms_b * 1e3, 2), "us_per_ciphertext": round(ms_b * 1e3 / nb, 2),
+                                   "keyswitch_per_s": round(nb * 1e3 / ms_b, 1)}
+        del ctb, outb, wsb
         R = 8
         gs = [galois[i % len(galois)] for i in range(R)]
         keys = ksk.unsqueeze(0).expand(R, *ksk.shape).contiguous()

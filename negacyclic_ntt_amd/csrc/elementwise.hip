@@ -160,6 +160,56 @@ __global__ __launch_bounds__(kThreads) void automorph_coeff_multi_kernel(uint64_
   for (uint32_t k = 0; k < P; k += 2) st_stream(out + idx + k, u64x2{v[k], v[k + 1]});
 }
 
+// Pair form of the same gather.  For an even output e, i = e h mod 2n is even, so the
+// input pair (i, i + 1) of the extended sequence in_ext = (in, -in) is one aligned
+// 16-byte load.  Its second element belongs to the output o = e + g mod 2n (since
+// (e + g) h = i + 1): out[o mod n], negated once more when o >= n (n h = n mod 2n).
+// As e runs over the even outputs, o mod n runs over the odd ones once each.  A
+// thread therefore reads one pair and writes two outputs: half the gather requests
+// of the per-element form, at the price of stores that fill half a line each (the
+// other half is the partner of another thread of the same limb, on the same XCD).
+// P pairs per thread; a block covers P * kThreads consecutive even outputs of one
+// row, so launched only when n / 2 is a multiple of that.
+#ifndef NNTT_AUTOMORPH_PAIR_NT
+#define NNTT_AUTOMORPH_PAIR_NT 0  // plain stores let the two halves of a line meet in L2 (non-temporal: +35%)
+#endif
+template <uint32_t P>
+__global__ __launch_bounds__(kThreads) void automorph_coeff_pair_kernel(uint64_t* __restrict__ out,
+                                                                        const uint64_t* __restrict__ in,
+                                                                        const ModInfo* __restrict__ mods,
+                                                                        uint32_t logn, uint32_t g, uint32_t h,
+                                                                        uint32_t num_limbs, uint32_t limb_begin,
+                                                                        uint32_t blocks_per_row) {
+  const uint32_t lb = xcd_local_block(blockIdx.x, gridDim.x);
+  const uint32_t n = 1u << logn, mask2n = 2 * n - 1;
+  const uint64_t row = lb / blocks_per_row;
+  const uint32_t pair0 = (lb % blocks_per_row) * (P * kThreads) + threadIdx.x;
+  const uint64_t q = mods[limb_begin + (uint32_t)(row % num_limbs)].q;
+  const uint64_t* src = in + (row << logn);
+  uint64_t* dst = out + (row << logn);
+  u64x2 v[P];
+  uint32_t e[P], i[P];
+#pragma unroll
+  for (uint32_t k = 0; k < P; ++k) {
+    e[k] = 2 * (pair0 + k * kThreads);
+    i[k] = (uint32_t)(((uint64_t)e[k] * h) & mask2n);
+    v[k] = *reinterpret_cast<const u64x2*>(src + (i[k] & (n - 1)));
+  }
+#pragma unroll
+  for (uint32_t k = 0; k < P; ++k) {
+    const bool neg0 = i[k] >= n;
+    const uint32_t o = (e[k] + g) & mask2n;
+    const bool neg1 = neg0 != (o >= n);
+#if NNTT_AUTOMORPH_PAIR_NT
+    __builtin_nontemporal_store(neg0 ? neg_mod(v[k].x, q) : v[k].x, dst + e[k]);
+    __builtin_nontemporal_store(neg1 ? neg_mod(v[k].y, q) : v[k].y, dst + (o & (n - 1)));
+#else
+    dst[e[k]] = neg0 ? neg_mod(v[k].x, q) : v[k].x;
+    dst[o & (n - 1)] = neg1 ? neg_mod(v[k].y, q) : v[k].y;
+#endif
+  }
+}
+
 // NTT domain (bit-reversed slots): out[k] = in[p(k)], 2 brv(p) + 1 = (2 brv(k) + 1) g mod 2n.
 __global__ __launch_bounds__(kThreads) void automorph_ntt_kernel(uint64_t* __restrict__ out,
                                                                  const uint64_t* __restrict__ in, uint32_t logn,
@@ -270,7 +320,25 @@ hipError_t launch_automorph(const ntt_plan* p, uint64_t* out, const uint64_t* in
 #define NNTT_AUTOMORPH_PER_THREAD 2  // measured on MI355X: 2 beats 1 by 12% and 4 by 5%
 #endif
     constexpr uint32_t kPer = NNTT_AUTOMORPH_PER_THREAD;
-    if (kPer > 1 && total % (kPer * kThreads) == 0)
+#ifndef NNTT_AUTOMORPH_PAIRS
+#define NNTT_AUTOMORPH_PAIRS 1  // pairs per thread (0: off).  MI355X, 2^16 x 384 rows: 97 us; 2: 102, 4: 106; per-element form: 114
+#endif
+    constexpr uint32_t kPairs = NNTT_AUTOMORPH_PAIRS;
+    constexpr uint32_t kPairBlock = (kPairs ? kPairs : 1) * kThreads;  // even outputs per block
+    const uint32_t half = p->n / 2, bpr = half / kPairBlock;
+    if (kPairs > 0 && bpr > 0 && half % kPairBlock == 0 && num_limbs <= 0xffffffffull / kThreads / bpr) {
+      // A launch holds at most 2^32 - 1 threads: split into launches of whole
+      // polynomials (a multiple of num_limbs rows, so each starts at limb_begin).
+      const uint64_t max_rows = (0xffffffffull / kThreads / bpr) / num_limbs * num_limbs;
+      for (uint64_t r0 = 0, rows_all = batch * num_limbs; r0 < rows_all;) {
+        const uint64_t rows = std::min<uint64_t>(rows_all - r0, max_rows);
+        const uint64_t off = r0 << p->logn;
+        hipLaunchKernelGGL(automorph_coeff_pair_kernel<kPairs ? kPairs : 1>, dim3((uint32_t)(rows * bpr)), dim3(kThreads), 0, s,
+                           out + off, in + off, p->d_mods, p->logn, (uint32_t)(g % two_n), h, num_limbs, limb_begin,
+                           bpr);
+        r0 += rows;
+      }
+    } else if (kPer > 1 && total % (kPer * kThreads) == 0)
       hipLaunchKernelGGL(automorph_coeff_multi_kernel<kPer>, dim3(blocks_for(total / kPer)), dim3(kThreads), 0, s,
                          out, in, p->d_mods, p->logn, h, num_limbs, limb_begin, total / kPer);
     else

@@ -144,7 +144,7 @@ def test_automorph_full_batch_and_ntt_commutation(B):
     assert_bits_equal(host(out), host(out2), "NTT-domain automorph commutes with the NTT")
 
 
-@pytest.mark.parametrize("logn", [1, 2, 5, 10, 13])
+@pytest.mark.parametrize("logn", [1, 2, 5, 9, 10, 11, 13])
 def test_automorph_small_rings(B, logn):
     n = 1 << logn
     ps = primes(30, 1 << 17, 2)
