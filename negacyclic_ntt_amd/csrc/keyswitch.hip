@@ -35,13 +35,25 @@ namespace nntt {
 namespace {
 
 constexpr int kKsThreads = 256;
+// Launch shapes measured on MI355X (n = 2^16, 24 + 8 primes below 2^60, dnum 3):
+// ModUp over all target primes in one group (the exact-width Garner chain needs no
+// extra waves: 28.8 us, two groups 29.6, four 40); ModDown in two groups of output
+// primes (one: 32, three: 30 us) whose loads are issued four limbs at a time (24.6 us;
+// eight: 25.7, twelve: 29.8).  Primes at or above 2^60 keep two ModUp groups.
 #ifndef NNTT_MODUP_GROUPS
-#define NNTT_MODUP_GROUPS 2
+#define NNTT_MODUP_GROUPS 1
+#endif
+#ifndef NNTT_MODUP_GROUPS_WIDE
+#define NNTT_MODUP_GROUPS_WIDE 2
+#endif
+#ifndef NNTT_MODDOWN_CH
+#define NNTT_MODDOWN_CH 4
 #endif
 #ifndef NNTT_MODDOWN_GROUPS
 #define NNTT_MODDOWN_GROUPS 2
 #endif
 constexpr uint32_t kModUpGroups = NNTT_MODUP_GROUPS;
+constexpr uint32_t kModUpGroupsWide = NNTT_MODUP_GROUPS_WIDE;
 constexpr uint32_t kModDownGroups = NNTT_MODDOWN_GROUPS;
 constexpr int kMaxDigitPrimes = 16;  // table row strides of the device constants
 constexpr int kMaxSpecial = 16;
@@ -203,11 +215,14 @@ struct KsDev {
 // product), so that the key product needs a single Montgomery reduction per output.
 // src: the polynomial that is decomposed, [batch][nq][n] with batch stride src_stride
 // (c1 of a ciphertext, or d2 of a tensor product).
-template <bool B60, int K>
+// EX = K: the launch has exactly K primes per digit, so the loops over them have
+// compile-time bounds (one straight-line block the scheduler can interleave).
+template <bool B60, int K, bool EX>
 __global__ __launch_bounds__(kKsThreads) void modup_kernel(uint64_t* __restrict__ ext,
                                                            const uint64_t* __restrict__ src, uint64_t src_stride,
                                                            KsDev kc, uint32_t logn, uint32_t h, uint32_t nq,
-                                                           uint32_t np_, uint32_t alpha, uint32_t dnum) {
+                                                           uint32_t np_, uint32_t alpha_arg, uint32_t dnum) {
+  const uint32_t alpha = EX ? (uint32_t)K : alpha_arg;
   const uint32_t n = 1u << logn;
   const uint32_t e = blockIdx.x * kKsThreads + threadIdx.x;
   if (e >= n) return;
@@ -387,13 +402,15 @@ __global__ __launch_bounds__(kKsThreads) void mac_hoisted_kernel(uint64_t* __res
 // grid.z = rotations x groups: rotation r (hoisted rotations; 0 otherwise) reads
 // acc + r acc_rot, writes out + r out_rot and gathers the additive input through
 // sigma with h = ha.h[r].
-template <bool B60, int KP>
+// EX = KP: exactly KP special primes (compile-time loop bounds, as in modup_kernel).
+template <bool B60, int KP, bool EX>
 __global__ __launch_bounds__(kKsThreads) void moddown_kernel(uint64_t* __restrict__ out,
                                                              const uint64_t* __restrict__ acc,
                                                              const uint64_t* __restrict__ add, uint64_t add_stride,
                                                              uint32_t add_mask, KsDev kc, uint32_t logn, uint32_t nq,
-                                                             uint32_t np_, uint32_t groups, uint64_t out_rot,
+                                                             uint32_t np_arg, uint32_t groups, uint64_t out_rot,
                                                              uint64_t acc_rot, HoistArgs ha) {
+  const uint32_t np_ = EX ? (uint32_t)KP : np_arg;
   const uint32_t n = 1u << logn;
   const uint32_t e = blockIdx.x * kKsThreads + threadIdx.x;
   if (e >= n) return;
@@ -418,7 +435,7 @@ __global__ __launch_bounds__(kKsThreads) void moddown_kernel(uint64_t* __restric
   const uint32_t l0 = grp * per, l1 = min(nq, l0 + per);
   // The output limbs go in chunks whose loads (accumulator residue, gathered addend)
   // are all issued together; the first chunk's before the Garner digits are computed.
-  constexpr int CH = 8;
+  constexpr int CH = NNTT_MODDOWN_CH;
   uint64_t av[CH], cv[CH];
   auto prefetch = [&](uint32_t lb) {
 #pragma unroll
@@ -715,17 +732,28 @@ int ks_check(const ntt_ks_plan* p, uint64_t* out, const KsIo& io, const uint64_t
   return NTT_OK;
 }
 
+#ifndef NNTT_KS_EXACT
+#define NNTT_KS_EXACT 1
+#endif
 template <bool B60, int K>
 void launch_modup(dim3 grid, hipStream_t s, uint64_t* ext, const KsIo& io, const ntt_ks_plan* p, uint32_t h) {
-  hipLaunchKernelGGL((modup_kernel<B60, K>), grid, dim3(kKsThreads), 0, s, ext, io.src, io.src_stride, p->dev,
-                     p->qp->logn, h, p->nq, p->np, p->alpha, p->dnum);
+  if (NNTT_KS_EXACT && p->alpha == (uint32_t)K)
+    hipLaunchKernelGGL((modup_kernel<B60, K, true>), grid, dim3(kKsThreads), 0, s, ext, io.src, io.src_stride,
+                       p->dev, p->qp->logn, h, p->nq, p->np, p->alpha, p->dnum);
+  else
+    hipLaunchKernelGGL((modup_kernel<B60, K, false>), grid, dim3(kKsThreads), 0, s, ext, io.src, io.src_stride,
+                       p->dev, p->qp->logn, h, p->nq, p->np, p->alpha, p->dnum);
 }
 
 template <bool B60, int KP>
 void launch_moddown(dim3 grid, hipStream_t s, uint64_t* out, const uint64_t* acc, const KsIo& io,
                     const ntt_ks_plan* p, uint32_t groups, uint64_t out_rot, uint64_t acc_rot, const HoistArgs& ha) {
-  hipLaunchKernelGGL((moddown_kernel<B60, KP>), grid, dim3(kKsThreads), 0, s, out, acc, io.add, io.add_stride,
-                     io.add_mask, p->dev, p->qp->logn, p->nq, p->np, groups, out_rot, acc_rot, ha);
+  if (NNTT_KS_EXACT && p->np == (uint32_t)KP)
+    hipLaunchKernelGGL((moddown_kernel<B60, KP, true>), grid, dim3(kKsThreads), 0, s, out, acc, io.add,
+                       io.add_stride, io.add_mask, p->dev, p->qp->logn, p->nq, p->np, groups, out_rot, acc_rot, ha);
+  else
+    hipLaunchKernelGGL((moddown_kernel<B60, KP, false>), grid, dim3(kKsThreads), 0, s, out, acc, io.add,
+                       io.add_stride, io.add_mask, p->dev, p->qp->logn, p->nq, p->np, groups, out_rot, acc_rot, ha);
 }
 
 constexpr uint64_t kMaxGridY = 65535;
@@ -736,9 +764,9 @@ constexpr uint64_t kMaxGridY = 65535;
 int ks_modup(const ntt_ks_plan* p, uint64_t* ext, const KsIo& io, uint32_t h, uint64_t batch, hipStream_t s) {
   const uint32_t n = p->qp->n, nqp = p->nq + p->np, dnum = p->dnum;
   const uint32_t tiles = (n + kKsThreads - 1) / kKsThreads;
-  // Groups of target primes per coefficient: enough resident waves to hide the
-  // latency of the long dependent Shoup chains (measured on MI355X).
-  const uint32_t up_groups = std::max(1u, std::min(kModUpGroups, nqp - p->alpha));
+  // Groups of target primes per coefficient (the Garner digits are recomputed per
+  // group): more resident waves for the longer Shoup chains at or above 2^60.
+  const uint32_t up_groups = std::max(1u, std::min(p->below60 ? kModUpGroups : kModUpGroupsWide, nqp - p->alpha));
   const uint64_t up_chunk = std::max<uint64_t>(1, kMaxGridY / dnum);
   for (uint64_t b0 = 0; b0 < batch; b0 += up_chunk) {
     const uint64_t nb = std::min(up_chunk, batch - b0);
