@@ -87,6 +87,7 @@ def parse():
     ap.add_argument("--rotate", type=int, default=3, help="distinct input sets cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-next-rows", action="store_true", help="skip relin / rescale / hoisted / modraise timings")
+    ap.add_argument("--no-other-configs", action="store_true", help="skip the n = 2^14 and n = 2048 workloads")
     ap.add_argument("--next-reps", type=int, default=10)
     ap.add_argument("--cpu-sample-limbs", type=int, default=384,
                     help="limbs of the batch the oracle processes for the CPU baseline (384 = all 16 polys)")
@@ -204,6 +205,123 @@ def next_rows(B, plan, ksp, ws, primes, W, KS, C, ct, ksk, galois, reps):
         out[f"modraise_{frm}_to_{L}"] = {"us": round(ms * 1e3, 2), "alg_GBps": round(byts / (ms * 1e-3) / 1e9, 1)}
         del x, y, mr
     return out
+
+
+def time_cycle(fns, reps):
+    """Mean milliseconds per call of fns[i % len(fns)] over `reps` calls (HIP events)."""
+    import torch
+    for f in fns[: min(len(fns), 3)]:
+        f()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        fns[i % len(fns)]()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def time_graph(fns, replays=5):
+    """Mean milliseconds per call when all of fns run inside one captured HIP graph."""
+    import torch
+    for f in fns:
+        f()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in fns:
+            f()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) / (replays * len(fns))
+
+
+def other_configs(B, reps):
+    """Per-call times on the three smaller workloads (their parity is tested; these
+    numbers are context, not part of `value`).  Operands rotate through copies of
+    about 1 GB in total so that the 256 MB Infinity Cache does not stand in for HBM.
+    The n = 2048 calls are also timed inside one HIP graph of many calls: their
+    launch latency exceeds their memory time."""
+    import torch
+    from negacyclic_ntt_amd import inputs, workloads
+    out = {}
+    r3 = lambda x: round(x, 3)
+
+    W = workloads.BATCH  # n = 2^14, 16 x 60-bit, 128 polynomials: NTT, pointwise, INTT
+    ps = B.find_primes(W.bits, W.n, W.limbs)
+    plan = B.Plan(W.n, ps, 0)
+    a = B.to_device(inputs.uniform_residues(W.shape_a, ps, W.seed_a))
+    b = B.to_device(inputs.uniform_residues(W.shape_a, ps, W.seed_b))
+    pairs = [(a, b), (a.clone(), b.clone())]
+    c = torch.empty_like(a)
+    limbs = a.numel() // W.n
+    f_ms = time_cycle([lambda x=x: B.ntt_forward(plan, x) for x, _ in pairs], reps)
+    p_ms = time_cycle([lambda x=x, y=y: B.poly_mul_ntt(plan, c, x, y) for x, y in pairs], reps)
+    i_ms = time_cycle([lambda x=x: B.ntt_inverse(plan, x) for x, _ in pairs], reps)
+    out[W.name] = {"ntt_forward_us": r3(f_ms * 1e3), "ntt_forward_limb_ntt_per_s": round(limbs / (f_ms * 1e-3)),
+                   "ntt_forward_alg_GBps": round(16 * a.numel() / (f_ms * 1e-3) / 1e9, 1),
+                   "poly_mul_us": r3(p_ms * 1e3), "poly_mul_alg_GBps": round(24 * a.numel() / (p_ms * 1e-3) / 1e9, 1),
+                   "ntt_inverse_us": r3(i_ms * 1e3), "ntt_inverse_limb_ntt_per_s": round(limbs / (i_ms * 1e-3))}
+    del pairs, a, b, c, plan
+
+    W = workloads.CHAIN  # n = 2048, 112 x 30-bit, 4 tokens x 2 components: NTT, tensor, INTT
+    ps = B.find_primes(W.bits, W.n, W.limbs)
+    plan = B.Plan(W.n, ps, 0)
+    a = B.to_device(inputs.uniform_residues(W.shape_a, ps, W.seed_a))
+    b = B.to_device(inputs.uniform_residues(W.shape_a, ps, W.seed_b))
+    copies = [(a, b)] + [(a.clone(), b.clone()) for _ in range(34)]  # 35 x 29 MB
+    d = torch.empty((W.shape_a[0], 3) + tuple(W.shape_a[2:]), dtype=torch.int64, device=a.device)
+    limbs = a.numel() // W.n
+    fwd = [lambda x=x: B.ntt_forward(plan, x) for x, _ in copies]
+    f_ms = time_cycle(fwd, max(reps, len(fwd)))
+    f_graph_ms = time_graph(fwd)
+    t_ms = time_cycle([lambda x=x, y=y: B.ct_tensor_ntt(plan, d, x, y) for x, y in copies], max(reps, len(copies)))
+    i_ms = time_cycle([lambda: B.ntt_inverse(plan, d)], reps)
+    out[W.name] = {"ntt_forward_us": r3(f_ms * 1e3), "ntt_forward_graph_us": r3(f_graph_ms * 1e3),
+                   "ntt_forward_limb_ntt_per_s": round(limbs / (f_ms * 1e-3)),
+                   "ntt_forward_graph_limb_ntt_per_s": round(limbs / (f_graph_ms * 1e-3)),
+                   "ct_tensor_us": r3(t_ms * 1e3),
+                   "ct_tensor_alg_GBps": round(56 * (a.numel() // 2) / (t_ms * 1e-3) / 1e9, 1),
+                   "ntt_inverse_of_tensor_us": r3(i_ms * 1e3),
+                   "ntt_inverse_limb_ntt_per_s": round(d.numel() // W.n / (i_ms * 1e-3))}
+    del copies, a, b, d, plan
+
+    W = workloads.POLYMUL  # n = 2048, 4 x 30-bit: NTT(A), NTT(B), pointwise, INTT
+    ps = B.find_primes(W.bits, W.n, W.limbs)
+    plan = B.Plan(W.n, ps, 0)
+    a = B.to_device(inputs.uniform_residues(W.shape_a, ps, W.seed_a))
+    b = B.to_device(inputs.uniform_residues(W.shape_a, ps, W.seed_b))
+    c = torch.empty_like(a)
+
+    def chain():
+        B.ntt_forward(plan, a)
+        B.ntt_forward(plan, b)
+        B.poly_mul_ntt(plan, c, a, b)
+        B.ntt_inverse(plan, c)
+    m_ms = time_cycle([chain], reps)
+    m_graph_ms = time_graph([chain] * 16)
+    out[W.name] = {"multiply_us": r3(m_ms * 1e3), "multiply_graph_us": r3(m_graph_ms * 1e3),
+                   "launches_per_multiply": 4}
+    return out
+
+
+def device_info():
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    info = {"name": p.name, "arch": getattr(p, "gcnArchName", None), "cus": p.multi_processor_count,
+            "hbm_GB": round(p.total_memory / 1e9, 1), "hip": torch.version.hip, "torch": torch.__version__}
+    clock = getattr(p, "clock_rate", None)
+    if clock:
+        info["clock_MHz"] = round(clock / 1e3)
+    return info
 
 
 def main():
@@ -369,8 +487,12 @@ def main():
         "roofline": roofline,
         "input_gen_s": round(gen_s, 2),
     }
+    out["device"] = device_info()
     if not args.no_next_rows:
         out["next_rows"] = next_rows(B, plan, ksp, ws, primes, W, KS, C, ct, ksk0, galois, args.next_reps)
+    if not args.no_other_configs:
+        del sets, keys, C, E, D
+        out["other_configs"] = other_configs(B, args.next_reps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(primes, n, nq, npr, dnum, args.cpu_sample_limbs, a_host, b_host,
                                            ct_host, ksk_host, galois[0])

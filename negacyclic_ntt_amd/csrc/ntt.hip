@@ -74,6 +74,12 @@ constexpr Sched make_sched(int logm) {
 #ifndef NNTT_LDS_PAD
 #define NNTT_LDS_PAD 1
 #endif
+#ifndef NNTT_LDS_BUF_ROWS1
+#define NNTT_LDS_BUF_ROWS1 1
+#endif
+#ifndef NNTT_SPLIT_MIN_LOGN
+#define NNTT_SPLIT_MIN_LOGN 15  // smallest ring that uses the two-pass split
+#endif
 template <class A>
 constexpr int sub_stride(int m) {
   return NNTT_LDS_PAD ? (1 << m) + ((1 << m) >> A::kPadShift) + 1 : (1 << m);
@@ -281,26 +287,46 @@ __global__ __launch_bounds__(LdsCfg<LOGN>::NT) void ntt_lds_kernel(uint64_t* dat
   uint64_t row0 = (uint64_t)blockIdx.x * ROWS;
   if (ROWS == 1) row0 = place_block(1, total_rows / num_limbs, num_limbs, 0).row;
 
-  // Coalesced load, two residues per thread per step.
+  // Coalesced load, two residues per thread per step.  Every load is issued before
+  // the first LDS write (a register buffer, no per-row branch), so that their
+  // latencies overlap.  A block's rows past the end re-read the last row: their
+  // LDS rows are transformed but never stored.
+  constexpr int kLoads = (ROWS * N) / (2 * NT);
   static_assert((ROWS * N) % (2 * NT) == 0, "whole iterations");
+  ulonglong2 buf[kLoads];
+  if constexpr (ROWS == 1 && !NNTT_LDS_BUF_ROWS1 && !GAL) {
 #pragma unroll
-  for (int it = 0; it < (ROWS * N) / (2 * NT); ++it) {
+    for (int it = 0; it < kLoads; ++it) {
+      const int e = 2 * tid + it * 2 * NT;
+      const ulonglong2 v = *reinterpret_cast<const ulonglong2*>(in + row0 * N + e);
+      lds[lpos<A>(e)] = (T)v.x;
+      lds[lpos<A>(e + 1)] = (T)v.y;
+    }
+  } else {
+#pragma unroll
+  for (int it = 0; it < kLoads; ++it) {
+    const int e = 2 * tid + it * 2 * NT;
+    const uint64_t r = min(row0 + (uint64_t)(e / N), total_rows - 1);
+    buf[it] = *reinterpret_cast<const ulonglong2*>(in + r * N + e % N);
+  }
+#pragma unroll
+  for (int it = 0; it < kLoads; ++it) {
     const int e = 2 * tid + it * 2 * NT;
     const int sub = e / N, pos = e % N;
-    if (row0 + sub < total_rows) {
-      const ulonglong2 v = *reinterpret_cast<const ulonglong2*>(in + (row0 + sub) * N + pos);
-      if (GAL) {
-        const T q = (T)mods[limb_begin + (uint32_t)((row0 + sub) % num_limbs)].q;
-        const uint32_t e0 = (uint32_t)(((uint64_t)pos * galois) & (2 * N - 1));
-        const uint32_t e1 = (uint32_t)(((uint64_t)(pos + 1) * galois) & (2 * N - 1));
-        const T x0 = (T)v.x, x1 = (T)v.y;
-        lds[sub * STRIDE + lpos<A>(e0 & (N - 1))] = e0 >= (uint32_t)N ? (x0 ? q - x0 : x0) : x0;
-        lds[sub * STRIDE + lpos<A>(e1 & (N - 1))] = e1 >= (uint32_t)N ? (x1 ? q - x1 : x1) : x1;
-      } else {
-        lds[sub * STRIDE + lpos<A>(pos)] = (T)v.x;
-        lds[sub * STRIDE + lpos<A>(pos + 1)] = (T)v.y;
-      }
+    const ulonglong2 v = buf[it];
+    if (GAL) {
+      const uint64_t r = min(row0 + (uint64_t)sub, total_rows - 1);
+      const T q = (T)mods[limb_begin + (uint32_t)(r % num_limbs)].q;
+      const uint32_t e0 = (uint32_t)(((uint64_t)pos * galois) & (2 * N - 1));
+      const uint32_t e1 = (uint32_t)(((uint64_t)(pos + 1) * galois) & (2 * N - 1));
+      const T x0 = (T)v.x, x1 = (T)v.y;
+      lds[sub * STRIDE + lpos<A>(e0 & (N - 1))] = e0 >= (uint32_t)N ? (x0 ? q - x0 : x0) : x0;
+      lds[sub * STRIDE + lpos<A>(e1 & (N - 1))] = e1 >= (uint32_t)N ? (x1 ? q - x1 : x1) : x1;
+    } else {
+      lds[sub * STRIDE + lpos<A>(pos)] = (T)v.x;
+      lds[sub * STRIDE + lpos<A>(pos + 1)] = (T)v.y;
     }
+  }
   }
   __syncthreads();
 
@@ -854,8 +880,18 @@ hipError_t launch_any(const ntt_plan* p, uint64_t* data, const uint64_t* in, uin
     NNTT_CASE(10)
     NNTT_CASE(11)
     NNTT_CASE(12)
+#if NNTT_SPLIT_MIN_LOGN > 13
     NNTT_CASE(13)
+#else
+    case 13:
+      return launch_split<A, 6, 7>(p, data, in, rows, limb_begin, num_limbs, op, g, s);
+#endif
+#if NNTT_SPLIT_MIN_LOGN > 14
     NNTT_CASE(14)
+#else
+    case 14:
+      return launch_split<A, 7, 7>(p, data, in, rows, limb_begin, num_limbs, op, g, s);
+#endif
 #undef NNTT_CASE
     case 15:
       return launch_split<A, 7, 8>(p, data, in, rows, limb_begin, num_limbs, op, g, s);
