@@ -186,6 +186,15 @@ int ntt_count_noncanonical(const ntt_plan *plan, const uint64_t *data, uint64_t 
  * before any launch, and this extends that to the values, at a cost. */
 void ntt_set_debug_checks(int on);
 
+/* Threads per kernel launch.  A dispatch packet holds at most 2^32 - 1 work-items
+ * per grid dimension, so calls whose grid would exceed the cap are split into
+ * several launches of whole polynomials (whole ciphertexts for ct_tensor_ntt), in
+ * order, on the caller's stream.  threads = 0 restores the default cap,
+ * 2^32 - 2^16; a smaller cap (at least 256) makes the splitting testable at small
+ * sizes.  Process-wide; NTT_EINVAL for 1..255.  A single polynomial whose
+ * launch alone exceeds the cap is NTT_EUNSUPPORTED. */
+int ntt_set_max_launch_threads(uint64_t threads);
+
 /* Key-switch plan over a Q u P basis: the first num_q primes of qp_plan form Q
  * and the next num_p form P (num_q + num_p <= primes in qp_plan); Q is split into
  * dnum digits of num_q / dnum consecutive primes (num_q % dnum == 0,

@@ -63,6 +63,7 @@ def lib():
             "rescale": (i32, [_VP, _VP, _VP, i32, u64, u32, u32, _VP]),
             "ntt_count_noncanonical": (i32, [_VP, _VP, u64, u32, u32, _VP, _VP]),
             "ntt_set_debug_checks": (None, [i32]),
+            "ntt_set_max_launch_threads": (i32, [u64]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -238,6 +239,12 @@ def count_noncanonical(plan: Plan, x, limb_begin: int = 0, stream=None) -> int:
 def set_debug_checks(on: bool):
     """Turn the library's input checks on or off for this process (see ntt_set_debug_checks)."""
     lib().ntt_set_debug_checks(1 if on else 0)
+
+
+def set_max_launch_threads(threads: int = 0):
+    """Cap the threads of one kernel launch (0: the hardware default); larger calls
+    are split into several launches (see ntt_set_max_launch_threads)."""
+    _check(lib().ntt_set_max_launch_threads(int(threads)), "ntt_set_max_launch_threads")
 
 
 def rescale(plan: Plan, out, x, mode: int = 0, limb_begin: int = 0, stream=None):

@@ -8,6 +8,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 
@@ -55,6 +56,19 @@ int debug_check_inputs(const ntt_plan* p, const uint64_t* data, uint64_t rows, u
 
 extern "C" void ntt_set_debug_checks(int on) { g_debug.store(on ? 1 : 0); }
 
+namespace nntt {
+namespace {
+std::atomic<uint64_t> g_max_threads{kMaxLaunchThreads};
+}
+uint64_t max_launch_threads() { return g_max_threads.load(std::memory_order_relaxed); }
+}  // namespace nntt
+
+extern "C" int ntt_set_max_launch_threads(uint64_t threads) {
+  if (threads != 0 && threads < 256) return NTT_EINVAL;
+  nntt::g_max_threads.store(threads == 0 ? nntt::kMaxLaunchThreads : std::min(threads, nntt::kMaxLaunchThreads));
+  return NTT_OK;
+}
+
 namespace {
 
 constexpr uint64_t kMaxElements = 1ull << 36;  // 512 GiB of residues: beyond any device
@@ -84,7 +98,10 @@ int check_plan_range(const ntt_plan* p, uint64_t batch, uint32_t limb_begin, uin
   return NTT_OK;
 }
 
-int status_of(hipError_t e) { return e == hipSuccess ? NTT_OK : NTT_EDEVICE; }
+// hipErrorNotSupported: a launcher's own refusal (one polynomial beyond the launch cap).
+int status_of(hipError_t e) {
+  return e == hipSuccess ? NTT_OK : e == hipErrorNotSupported ? NTT_EUNSUPPORTED : NTT_EDEVICE;
+}
 
 int transform(const ntt_plan* p, uint64_t* data, uint64_t batch, uint32_t limb_begin, uint32_t num_limbs,
               void* stream, bool inverse) {

@@ -289,75 +289,87 @@ __global__ void zero_counter_kernel(unsigned long long* count) { *count = 0; }
 
 uint32_t blocks_for(uint64_t work) { return (uint32_t)((work + kThreads - 1) / kThreads); }
 
+// launch(first, count) over items [0, items) in parts that keep each launch within
+// the launch cap, given the threads one item needs.
+template <class F>
+hipError_t in_parts(uint64_t items, uint64_t threads_per_item, F&& launch) {
+  const uint64_t per = items_per_launch(threads_per_item);
+  if (per == 0) return hipErrorNotSupported;
+  for (uint64_t i0 = 0; i0 < items; i0 += per) {
+    launch(i0, std::min(per, items - i0));
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 }  // namespace
 
 hipError_t launch_pointwise(const ntt_plan* p, uint64_t* out, const uint64_t* a, const uint64_t* b, uint64_t batch,
                             uint32_t limb_begin, uint32_t num_limbs, hipStream_t s) {
-  const uint64_t pairs = (batch * num_limbs * p->n) / 2;
-  if (!pairs) return hipSuccess;
-  hipLaunchKernelGGL(pointwise_kernel, dim3(blocks_for(pairs)), dim3(kThreads), 0, s, out, a, b, p->d_mods, p->logn,
-                     num_limbs, limb_begin, pairs);
-  return hipGetLastError();
+  const uint64_t poly = (uint64_t)num_limbs * p->n;  // elements per polynomial
+  return in_parts(batch, poly / 2, [&](uint64_t b0, uint64_t nb) {
+    const uint64_t off = b0 * poly, pairs = nb * poly / 2;
+    hipLaunchKernelGGL(pointwise_kernel, dim3(blocks_for(pairs)), dim3(kThreads), 0, s, out + off, a + off, b + off,
+                       p->d_mods, p->logn, num_limbs, limb_begin, pairs);
+  });
 }
 
 hipError_t launch_tensor(const ntt_plan* p, uint64_t* out, const uint64_t* a, const uint64_t* b, uint64_t batch,
                          uint32_t limb_begin, uint32_t num_limbs, hipStream_t s) {
-  const uint64_t pairs = (batch * num_limbs * p->n) / 2;
-  if (!pairs) return hipSuccess;
-  hipLaunchKernelGGL(tensor_kernel, dim3(blocks_for(pairs)), dim3(kThreads), 0, s, out, a, b, p->d_mods, p->logn,
-                     num_limbs, limb_begin, pairs);
-  return hipGetLastError();
+  const uint64_t plane = (uint64_t)num_limbs * p->n;  // elements per component
+  return in_parts(batch, plane / 2, [&](uint64_t b0, uint64_t nb) {
+    const uint64_t pairs = nb * plane / 2;
+    hipLaunchKernelGGL(tensor_kernel, dim3(blocks_for(pairs)), dim3(kThreads), 0, s, out + b0 * 3 * plane,
+                       a + b0 * 2 * plane, b + b0 * 2 * plane, p->d_mods, p->logn, num_limbs, limb_begin, pairs);
+  });
 }
 
 hipError_t launch_automorph(const ntt_plan* p, uint64_t* out, const uint64_t* in, uint64_t g, int domain,
                             uint64_t batch, uint32_t limb_begin, uint32_t num_limbs, hipStream_t s) {
-  const uint64_t total = batch * num_limbs * p->n;
-  if (!total) return hipSuccess;
+  const uint64_t poly = (uint64_t)num_limbs * p->n;  // elements per polynomial
+  if (batch * poly == 0) return hipSuccess;
   const uint32_t two_n = 2 * p->n;
-  if (domain == 0) {
-    const uint32_t h = (uint32_t)host_invmod(g % two_n, two_n);
+  if (domain != 0)
+    return in_parts(batch, poly, [&](uint64_t b0, uint64_t nb) {
+      hipLaunchKernelGGL(automorph_ntt_kernel, dim3(blocks_for(nb * poly)), dim3(kThreads), 0, s, out + b0 * poly,
+                         in + b0 * poly, p->logn, (uint32_t)(g % two_n), nb * poly);
+    });
+  const uint32_t h = (uint32_t)host_invmod(g % two_n, two_n);
 #ifndef NNTT_AUTOMORPH_PER_THREAD
 #define NNTT_AUTOMORPH_PER_THREAD 2  // measured on MI355X: 2 beats 1 by 12% and 4 by 5%
 #endif
-    constexpr uint32_t kPer = NNTT_AUTOMORPH_PER_THREAD;
+  constexpr uint32_t kPer = NNTT_AUTOMORPH_PER_THREAD;
 #ifndef NNTT_AUTOMORPH_PAIRS
 #define NNTT_AUTOMORPH_PAIRS 1  // pairs per thread (0: off).  MI355X, 2^16 x 384 rows: 97 us; 2: 102, 4: 106; per-element form: 114
 #endif
-    constexpr uint32_t kPairs = NNTT_AUTOMORPH_PAIRS;
-    constexpr uint32_t kPairBlock = (kPairs ? kPairs : 1) * kThreads;  // even outputs per block
-    const uint32_t half = p->n / 2, bpr = half / kPairBlock;
-    if (kPairs > 0 && bpr > 0 && half % kPairBlock == 0 && num_limbs <= 0xffffffffull / kThreads / bpr) {
-      // A launch holds at most 2^32 - 1 threads: split into launches of whole
-      // polynomials (a multiple of num_limbs rows, so each starts at limb_begin).
-      const uint64_t max_rows = (0xffffffffull / kThreads / bpr) / num_limbs * num_limbs;
-      for (uint64_t r0 = 0, rows_all = batch * num_limbs; r0 < rows_all;) {
-        const uint64_t rows = std::min<uint64_t>(rows_all - r0, max_rows);
-        const uint64_t off = r0 << p->logn;
-        hipLaunchKernelGGL(automorph_coeff_pair_kernel<kPairs ? kPairs : 1>, dim3((uint32_t)(rows * bpr)), dim3(kThreads), 0, s,
-                           out + off, in + off, p->d_mods, p->logn, (uint32_t)(g % two_n), h, num_limbs, limb_begin,
-                           bpr);
-        r0 += rows;
-      }
-    } else if (kPer > 1 && total % (kPer * kThreads) == 0)
+  constexpr uint32_t kPairs = NNTT_AUTOMORPH_PAIRS;
+  constexpr uint32_t kPairBlock = (kPairs ? kPairs : 1) * kThreads;  // even outputs per block
+  const uint32_t half = p->n / 2, bpr = half / kPairBlock;
+  if (kPairs > 0 && bpr > 0 && half % kPairBlock == 0)
+    return in_parts(batch, (uint64_t)num_limbs * bpr * kThreads, [&](uint64_t b0, uint64_t nb) {
+      hipLaunchKernelGGL(automorph_coeff_pair_kernel<kPairs ? kPairs : 1>, dim3((uint32_t)(nb * num_limbs * bpr)),
+                         dim3(kThreads), 0, s, out + b0 * poly, in + b0 * poly, p->d_mods, p->logn,
+                         (uint32_t)(g % two_n), h, num_limbs, limb_begin, bpr);
+    });
+  return in_parts(batch, poly, [&](uint64_t b0, uint64_t nb) {
+    const uint64_t total = nb * poly;
+    if (kPer > 1 && total % (kPer * kThreads) == 0)
       hipLaunchKernelGGL(automorph_coeff_multi_kernel<kPer>, dim3(blocks_for(total / kPer)), dim3(kThreads), 0, s,
-                         out, in, p->d_mods, p->logn, h, num_limbs, limb_begin, total / kPer);
+                         out + b0 * poly, in + b0 * poly, p->d_mods, p->logn, h, num_limbs, limb_begin, total / kPer);
     else
-      hipLaunchKernelGGL(automorph_coeff_kernel, dim3(blocks_for(total)), dim3(kThreads), 0, s, out, in, p->d_mods,
-                         p->logn, h, num_limbs, limb_begin, total);
-  } else {
-    hipLaunchKernelGGL(automorph_ntt_kernel, dim3(blocks_for(total)), dim3(kThreads), 0, s, out, in, p->logn,
-                       (uint32_t)(g % two_n), total);
-  }
-  return hipGetLastError();
+      hipLaunchKernelGGL(automorph_coeff_kernel, dim3(blocks_for(total)), dim3(kThreads), 0, s, out + b0 * poly,
+                         in + b0 * poly, p->d_mods, p->logn, h, num_limbs, limb_begin, total);
+  });
 }
 
 hipError_t launch_count_noncanonical(const ntt_plan* p, const uint64_t* data, uint64_t rows, uint32_t limb_begin,
                                      uint32_t num_limbs, unsigned long long* count, hipStream_t s) {
-  const uint64_t total = rows * num_limbs * p->n;
-  if (!total) return hipSuccess;
-  hipLaunchKernelGGL(count_noncanonical_kernel, dim3(blocks_for(total)), dim3(kThreads), 0, s, data, p->d_mods,
-                     p->logn, num_limbs, limb_begin, total, count);
-  return hipGetLastError();
+  const uint64_t poly = (uint64_t)num_limbs * p->n;
+  return in_parts(rows, poly, [&](uint64_t r0, uint64_t nr) {
+    hipLaunchKernelGGL(count_noncanonical_kernel, dim3(blocks_for(nr * poly)), dim3(kThreads), 0, s,
+                       data + r0 * poly, p->d_mods, p->logn, num_limbs, limb_begin, nr * poly, count);
+  });
 }
 
 hipError_t launch_zero_counter(unsigned long long* count, hipStream_t s) {

@@ -91,7 +91,20 @@ struct DeviceGuard {
   ~DeviceGuard();
 };
 
-// Launchers (ntt.hip). Arguments already validated. Return the launch status.
+// Threads of one launch: a dispatch packet holds at most 2^32 - 1 work-items per
+// grid dimension.  max_launch_threads() is this cap, or the smaller one set through
+// ntt_set_max_launch_threads (capi.cpp).
+// The default cap leaves room for the rounding up of a launch to whole workgroups.
+constexpr uint64_t kMaxLaunchThreads = 0xffff0000ull;
+uint64_t max_launch_threads();
+// Items (polynomials, ciphertexts) per launch when each needs `threads_per_item`
+// threads; 0 when one item alone exceeds the cap.
+inline uint64_t items_per_launch(uint64_t threads_per_item) {
+  return threads_per_item ? max_launch_threads() / threads_per_item : 0;
+}
+
+// Launchers (ntt.hip). Arguments already validated. Return the launch status
+// (hipErrorInvalidConfiguration when one polynomial exceeds the launch cap).
 hipError_t launch_ntt(const ntt_plan* p, uint64_t* data, uint64_t batch, uint32_t limb_begin, uint32_t num_limbs,
                       bool inverse, hipStream_t s);
 hipError_t launch_ntt_galois(const ntt_plan* p, uint64_t* out, const uint64_t* in, uint64_t g, uint64_t batch,

@@ -29,6 +29,8 @@
 // in registers and runs r stages on it; sets are exchanged through LDS between
 // passes.  LDS rows are padded by one slot per 128 bytes so strided set accesses
 // spread over the banks.
+#include <algorithm>
+
 #include "internal.h"
 
 namespace nntt {
@@ -902,15 +904,23 @@ hipError_t launch_any(const ntt_plan* p, uint64_t* data, const uint64_t* in, uin
   }
 }
 
+// Every transform kernel runs at most n / 2 threads per limb, so a launch of whole
+// polynomials stays within the launch cap; larger batches go in several launches.
 hipError_t dispatch(const ntt_plan* p, uint64_t* data, const uint64_t* in, uint64_t batch, uint32_t limb_begin,
                     uint32_t num_limbs, Op op, uint32_t g, hipStream_t s) {
-  const uint64_t rows = batch * num_limbs;
-  if (rows == 0) return hipSuccess;
-  if (range_is_narrow(p, limb_begin, num_limbs))
-    return launch_any<Narrow>(p, data, in, rows, limb_begin, num_limbs, op, g, s);
-  if (range_below60(p, limb_begin, num_limbs))
-    return launch_any<Wide60>(p, data, in, rows, limb_begin, num_limbs, op, g, s);
-  return launch_any<Wide>(p, data, in, rows, limb_begin, num_limbs, op, g, s);
+  if (batch * num_limbs == 0) return hipSuccess;
+  const uint64_t per = items_per_launch((uint64_t)num_limbs * std::max<uint32_t>(1, p->n / 2));
+  if (per == 0) return hipErrorNotSupported;
+  const bool narrow = range_is_narrow(p, limb_begin, num_limbs), b60 = range_below60(p, limb_begin, num_limbs);
+  for (uint64_t b0 = 0; b0 < batch; b0 += per) {
+    const uint64_t rows = std::min(per, batch - b0) * num_limbs, off = b0 * num_limbs * p->n;
+    hipError_t e;
+    if (narrow) e = launch_any<Narrow>(p, data + off, in + off, rows, limb_begin, num_limbs, op, g, s);
+    else if (b60) e = launch_any<Wide60>(p, data + off, in + off, rows, limb_begin, num_limbs, op, g, s);
+    else e = launch_any<Wide>(p, data + off, in + off, rows, limb_begin, num_limbs, op, g, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace

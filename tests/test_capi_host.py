@@ -159,3 +159,12 @@ def test_plan_info():
     v = ctypes.c_uint64()
     assert B.lib().ntt_plan_prime(plan.handle, 2, ctypes.byref(v)) == 0 and v.value == q[2]
     assert B.lib().ntt_plan_prime(plan.handle, 3, ctypes.byref(v)) == B.NTT_EINVAL
+
+
+def test_launch_cap_setter():
+    L = B.lib()
+    assert L.ntt_set_max_launch_threads(1) == B.NTT_EINVAL
+    assert L.ntt_set_max_launch_threads(255) == B.NTT_EINVAL
+    assert L.ntt_set_max_launch_threads(256) == B.NTT_OK
+    assert L.ntt_set_max_launch_threads(1 << 40) == B.NTT_OK  # clamped to the hardware cap
+    assert L.ntt_set_max_launch_threads(0) == B.NTT_OK

@@ -233,3 +233,68 @@ def test_count_noncanonical_and_debug_checks():
         B.set_debug_checks(False)
     assert L.ntt_forward(plan.handle, V(tb.data_ptr()), 2, 0, 4, None) == B.NTT_OK  # checks off: it runs
     torch.cuda.synchronize()
+
+
+def _cap_case(B, logn):
+    """Every one-dimensional launch is split into parts of whole polynomials (or
+    ciphertexts) under a small launch cap; the results match the oracle, with a batch
+    that leaves a ragged last part."""
+    import torch
+    n, L, batch = 1 << logn, 3, 7
+    ps = primes(30 if logn < 8 else 60, 2 * n, L)
+    plan = B.Plan(n, ps, 0)
+    a = residues((batch, 2, L, n), ps, 9700 + logn)
+    b = residues((batch, 2, L, n), ps, 9800 + logn)
+    fa = orc.batch_ntt(a, ps)
+    fb = orc.batch_ntt(b, ps)
+    g = 5 % (2 * n)
+    # n / 2 threads per limb and polynomial at most: a cap of L n threads admits two
+    # polynomials (one ciphertext) per launch for n = 1024, five for n = 32
+    B.set_max_launch_threads(max(256, L * n))
+    try:
+        ta = dev(a)
+        B.ntt_forward(plan, ta)
+        assert_bits_equal(host(ta), fa, "forward")
+        tg = torch.empty_like(ta)
+        B.ntt_forward_galois(plan, tg, dev(a), g)
+        assert_bits_equal(host(tg), orc.batch_ntt(orc.batch_automorph(a, g, 0, ps), ps), "forward galois")
+        tb = dev(fb)
+        tc = B.poly_mul_ntt(plan, torch.empty_like(ta), ta, tb)
+        assert_bits_equal(host(tc), orc.batch_pointwise(fa, fb, ps), "pointwise")
+        td = torch.empty((batch, 3, L, n), dtype=torch.int64, device=ta.device)
+        B.ct_tensor_ntt(plan, td, ta, tb)
+        assert_bits_equal(host(td), orc.batch_tensor(fa, fb, ps), "tensor")
+        B.ntt_inverse(plan, ta)
+        assert_bits_equal(host(ta), a, "inverse")
+        for domain in (0, 1):
+            src = a if domain == 0 else fa
+            out = torch.empty_like(ta)
+            B.automorph(plan, out, dev(src), g, domain)
+            assert_bits_equal(host(out), orc.batch_automorph(src, g, domain, ps), f"automorph domain {domain}")
+        assert B.count_noncanonical(plan, dev(a)) == 0
+    finally:
+        B.set_max_launch_threads(0)
+
+
+@pytest.mark.parametrize("logn", [5, 10])
+def test_launch_cap_splits_every_launch(B, logn):
+    announce("launch cap", logn)
+    _cap_case(B, logn)
+
+
+def test_launch_cap_too_small_for_one_polynomial(B):
+    import torch
+    n, L = 1 << 12, 4
+    ps = primes(60, 2 * n, L)
+    plan = B.Plan(n, ps, 0)
+    x = dev(residues((2, L, n), ps, 9900))
+    B.set_max_launch_threads(256)  # one polynomial needs L n / 2 threads
+    try:
+        with pytest.raises(B.NttError) as ei:
+            B.ntt_forward(plan, x)
+        assert ei.value.status == B.NTT_EUNSUPPORTED
+        with pytest.raises(B.NttError):
+            B.poly_mul_ntt(plan, torch.empty_like(x), x, x)
+    finally:
+        B.set_max_launch_threads(0)
+    B.ntt_forward(plan, x)  # the default cap is back
