@@ -81,6 +81,20 @@ def test_prime_lists_are_the_first_descending(w, primes):
         c -= two_n
 
 
+def test_prime_search_small_brute_force():
+    """Every prime below 2^bits that is 1 mod 2n, largest first, by trial division,
+    for widths where the largest candidate is itself prime (2^4: 13 = 3 * 4 + 1)."""
+    def trial(n):
+        return n >= 2 and all(n % d for d in range(2, int(n ** 0.5) + 1))
+
+    for bits in range(3, 17):
+        for two_n in (4, 8, 16, 32, 64):
+            want = [c for c in range((1 << bits) - 1, 1, -1) if c % two_n == 1 and trial(c)]
+            got = orc.find_primes(bits, two_n, len(want)) if want else []
+            assert got == want, (bits, two_n)
+    assert orc.find_primes(4, 4, 2) == [13, 5]
+
+
 # ---- P2: psi --------------------------------------------------------------------
 
 @pytest.mark.parametrize("w", workloads.ALL, ids=lambda w: w.name)
@@ -727,3 +741,11 @@ def test_modraise_decrypts_modulo_the_low_modulus(ks_primes):
     for a, b in zip(full, low):
         assert (a - b) % q0 == 0
         assert abs((a - b) // q0) <= l1 + 1
+
+
+def test_a_planted_mistake_fails_a_pin():
+    """The mutation driver (tests/oracle_mutations.py, all mutants on demand) on one
+    representative: the forward butterfly's difference turned into a sum."""
+    import tests.oracle_mutations as mut
+    idx = [i for i, m in enumerate(mut.MUTANTS) if m[0].startswith("forward butterfly")][0]
+    assert mut.run_mutant(idx).startswith("killed")
