@@ -42,9 +42,10 @@
  *             "Value signatures and reusable buffers", section "The writer cannot
  *             infer arbitrary readers").
  *   Errors.   Arguments are validated before anything is launched (FHElium,
- *             section "Schema registration and device dispatch"); on a negative
- *             status nothing was enqueued.  NTT_EDEVICE also reports a failed
- *             launch.
+ *             section "Schema registration and device dispatch"): NTT_EINVAL,
+ *             NTT_EUNSUPPORTED and NTT_EOVERLAP mean nothing was enqueued.
+ *             NTT_EDEVICE also reports a failed launch; launches of the same call
+ *             that preceded it (a call may take several) stay enqueued.
  *   Threads.  Plans are immutable after creation; concurrent calls on different
  *             streams are safe when their output and workspace buffers differ.
  */
@@ -220,9 +221,10 @@ int keyswitch_workspace_size(const ntt_ks_plan *plan, uint64_t batch, size_t *by
  * and kestrel-llm, section 4.2) and reduced onto every other prime.  ModDown is
  * the exact floor: out = floor(X / P) mod q for the integer X in [0, QP) with
  * the accumulator's residues (FHElium's "QP-to-Q ModDown").
- * galois_elt odd and < 2n (1 = no rotation, a plain key-switch).  workspace:
- * device buffer of at least keyswitch_workspace_size bytes, 256-byte aligned,
- * not overlapping out/ct/ksk.  out must not overlap ct, ksk or workspace. */
+ * galois_elt odd and < 2n (1 = no rotation, a plain key-switch).  batch <= 4096
+ * (NTT_EUNSUPPORTED beyond).  workspace: device buffer of at least
+ * keyswitch_workspace_size bytes, 256-byte aligned, not overlapping out/ct/ksk.
+ * out must not overlap ct, ksk or workspace. */
 int keyswitch(const ntt_ks_plan *plan, uint64_t *out, const uint64_t *ct, const uint64_t *ksk,
               uint64_t galois_elt, uint64_t batch, void *workspace, size_t workspace_bytes, void *stream);
 
@@ -246,8 +248,8 @@ int keyswitch_hoisted_workspace_size(const ntt_ks_plan *plan, uint32_t num_rot, 
  * sigma_g(c1): where sigma_g flips a coefficient's sign they differ by the digit
  * modulus, so the result differs from keyswitch() by a valid re-encryption of the
  * same value (both decompositions satisfy the same congruence and bound).
- * dnum <= 16.  workspace: keyswitch_hoisted_workspace_size bytes, 256-byte
- * aligned.  out must not overlap ct, ksk or workspace. */
+ * dnum <= 16, batch <= 4096.  workspace: keyswitch_hoisted_workspace_size bytes,
+ * 256-byte aligned.  out must not overlap ct, ksk or workspace. */
 int keyswitch_hoisted(const ntt_ks_plan *plan, uint64_t *out, const uint64_t *ct, const uint64_t *ksk,
                       const uint64_t *galois_elts, uint32_t num_rot, uint64_t batch, void *workspace,
                       size_t workspace_bytes, void *stream);
@@ -261,8 +263,8 @@ int keyswitch_hoisted(const ntt_ks_plan *plan, uint64_t *out, const uint64_t *ct
  *   out : [batch][2][num_q][n] = ( d0 + ModDown(acc_0), d1 + ModDown(acc_1) ) with
  *         acc_c = INTT( sum_j NTT(ModUp(digit_j(d2))) * rlk[j][c] ).
  * The same ModUp / key product / ModDown as keyswitch with no automorphism.
- * workspace: as for keyswitch (keyswitch_workspace_size bytes for `batch`).  out
- * must not overlap d, rlk or workspace (NTT_EOVERLAP). */
+ * batch <= 4096.  workspace: as for keyswitch (keyswitch_workspace_size bytes for
+ * `batch`).  out must not overlap d, rlk or workspace (NTT_EOVERLAP). */
 int relinearize(const ntt_ks_plan *plan, uint64_t *out, const uint64_t *d, const uint64_t *rlk, uint64_t batch,
                 void *workspace, size_t workspace_bytes, void *stream);
 
