@@ -76,9 +76,6 @@ constexpr Sched make_sched(int logm) {
 #ifndef NNTT_LDS_PAD
 #define NNTT_LDS_PAD 1
 #endif
-#ifndef NNTT_LDS_BUF_ROWS1
-#define NNTT_LDS_BUF_ROWS1 1
-#endif
 #ifndef NNTT_SPLIT_MIN_LOGN
 #define NNTT_SPLIT_MIN_LOGN 15  // smallest ring that uses the two-pass split
 #endif
@@ -310,15 +307,6 @@ __global__ __launch_bounds__(LdsCfg<LOGN>::NT) void ntt_lds_kernel(uint64_t* dat
   constexpr int kLoads = (ROWS * N) / (2 * NT);
   static_assert((ROWS * N) % (2 * NT) == 0, "whole iterations");
   ulonglong2 buf[kLoads];
-  if constexpr (ROWS == 1 && !NNTT_LDS_BUF_ROWS1 && !GAL) {
-#pragma unroll
-    for (int it = 0; it < kLoads; ++it) {
-      const int e = 2 * tid + it * 2 * NT;
-      const ulonglong2 v = *reinterpret_cast<const ulonglong2*>(in + row0 * N + e);
-      lds[lpos<A>(e)] = (T)v.x;
-      lds[lpos<A>(e + 1)] = (T)v.y;
-    }
-  } else {
 #pragma unroll
   for (int it = 0; it < kLoads; ++it) {
     const int e = 2 * tid + it * 2 * NT;
@@ -342,7 +330,6 @@ __global__ __launch_bounds__(LdsCfg<LOGN>::NT) void ntt_lds_kernel(uint64_t* dat
       lds[sub * STRIDE + lpos<A>(pos)] = (T)v.x;
       lds[sub * STRIDE + lpos<A>(pos + 1)] = (T)v.y;
     }
-  }
   }
   __syncthreads();
 
