@@ -562,6 +562,21 @@ struct MacSrc {
   uint32_t dnum, chunk;
 };
 
+// Key residues are read once per launch: non-temporal loads keep them from evicting
+// the digits, which the hoisted product reads once per rotation and component.
+#ifndef NNTT_MAC_KEY_NT
+#define NNTT_MAC_KEY_NT 1
+#endif
+__device__ __forceinline__ ulonglong2 load_key(const uint64_t* p) {
+#if NNTT_MAC_KEY_NT
+  typedef unsigned long long u64x2_t __attribute__((ext_vector_type(2)));
+  const u64x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u64x2_t*>(p));
+  return ulonglong2{v.x, v.y};
+#else
+  return *reinterpret_cast<const ulonglong2*>(p);
+#endif
+}
+
 // DN > 0: dnum == DN and DN products fit one reduction (all loads of an element pair
 // are issued before any arithmetic); DN == 0: any dnum, chunked reductions.
 template <class A, int LOGN1, int LOGN2, int DN>
@@ -598,7 +613,7 @@ __global__ __launch_bounds__(RowCfg<LOGN2>::NT) void ntt_row_mac_kernel(uint64_t
 #pragma unroll
       for (int j = 0; j < DN; ++j) {
         d[j] = *reinterpret_cast<const ulonglong2*>(xe + j * plane + e);
-        k[j] = *reinterpret_cast<const ulonglong2*>(kk + 2 * j * plane + e);
+        k[j] = load_key(kk + 2 * j * plane + e);
       }
 #pragma unroll
       for (int j = 0; j < DN; ++j) {
@@ -611,7 +626,7 @@ __global__ __launch_bounds__(RowCfg<LOGN2>::NT) void ntt_row_mac_kernel(uint64_t
     uint32_t c = 0;
     for (uint32_t j = 0; j < ms.dnum; ++j) {
       const ulonglong2 d = *reinterpret_cast<const ulonglong2*>(xe + j * plane + e);
-      const ulonglong2 k = *reinterpret_cast<const ulonglong2*>(kk + 2 * j * plane + e);
+      const ulonglong2 k = load_key(kk + 2 * j * plane + e);
       mac128(a0, d.x, k.x);
       mac128(a1, d.y, k.y);
       if (++c == ms.chunk || j + 1 == ms.dnum) {
@@ -695,7 +710,7 @@ __global__ __launch_bounds__(RowCfg<LOGN2>::NT) void ntt_row_mac_hoisted_kernel(
       for (int j = 0; j < DN; ++j) {
         d0[j] = xe[j * plane + s0];
         d1[j] = xe[j * plane + s1];
-        k[j] = *reinterpret_cast<const ulonglong2*>(kk + 2 * j * plane + e);
+        k[j] = load_key(kk + 2 * j * plane + e);
       }
 #pragma unroll
       for (int j = 0; j < DN; ++j) {
@@ -707,7 +722,7 @@ __global__ __launch_bounds__(RowCfg<LOGN2>::NT) void ntt_row_mac_hoisted_kernel(
     } else {
       uint32_t c = 0;
       for (uint32_t j = 0; j < ms.dnum; ++j) {
-        const ulonglong2 k = *reinterpret_cast<const ulonglong2*>(kk + 2 * j * plane + e);
+        const ulonglong2 k = load_key(kk + 2 * j * plane + e);
         mac128(a0, xe[j * plane + s0], k.x);
         mac128(a1, xe[j * plane + s1], k.y);
         if (++c == ms.chunk || j + 1 == ms.dnum) {
