@@ -360,6 +360,18 @@ __global__ __launch_bounds__(LdsCfg<LOGN>::NT) void ntt_lds_kernel(uint64_t* dat
   }
 }
 
+// A 16-byte load, non-temporal when NT (data read once per launch).
+template <bool NT>
+__device__ __forceinline__ ulonglong2 load_tile(const uint64_t* p) {
+  if constexpr (NT) {
+    typedef unsigned long long u64x2_t __attribute__((ext_vector_type(2)));
+    const u64x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u64x2_t*>(p));
+    return ulonglong2{v.x, v.y};
+  } else {
+    return *reinterpret_cast<const ulonglong2*>(p);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Two-pass split for n = N1 * N2 (N2 contiguous).  Column kernel: a workgroup
 // owns COLS adjacent columns (COLS * 8 B = one 128 B line per row) of one limb.
@@ -567,15 +579,7 @@ struct MacSrc {
 #ifndef NNTT_MAC_KEY_NT
 #define NNTT_MAC_KEY_NT 1
 #endif
-__device__ __forceinline__ ulonglong2 load_key(const uint64_t* p) {
-#if NNTT_MAC_KEY_NT
-  typedef unsigned long long u64x2_t __attribute__((ext_vector_type(2)));
-  const u64x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u64x2_t*>(p));
-  return ulonglong2{v.x, v.y};
-#else
-  return *reinterpret_cast<const ulonglong2*>(p);
-#endif
-}
+__device__ __forceinline__ ulonglong2 load_key(const uint64_t* p) { return load_tile<NNTT_MAC_KEY_NT != 0>(p); }
 
 // DN > 0: dnum == DN and DN products fit one reduction (all loads of an element pair
 // are issued before any arithmetic); DN == 0: any dnum, chunked reductions.
