@@ -28,17 +28,6 @@ __device__ __forceinline__ void st_stream(uint64_t* p, u64x2 v) {
   __builtin_nontemporal_store(v, reinterpret_cast<u64x2*>(p));
 }
 
-// Blocks are dispatched round-robin over the 8 XCDs of an MI355X; this maps the
-// hardware block id to a logical id so that each XCD works on one contiguous
-// range of logical blocks (and hence of the tensor), keeping its L2 working set
-// local.  Identity for the tail that does not fill all eight.
-__device__ __forceinline__ uint32_t xcd_local_block(uint32_t b, uint32_t nblocks) {
-  constexpr uint32_t kXcd = 8;
-  const uint32_t full = nblocks - nblocks % kXcd;
-  if (b >= full) return b;
-  return (b % kXcd) * (full / kXcd) + b / kXcd;
-}
-
 __global__ __launch_bounds__(kThreads) void pointwise_kernel(uint64_t* __restrict__ out,
                                                              const uint64_t* __restrict__ a,
                                                              const uint64_t* __restrict__ b,

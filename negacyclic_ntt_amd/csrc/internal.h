@@ -83,6 +83,17 @@ uint64_t host_invmod(uint64_t a, uint64_t q);
 bool host_is_prime(uint64_t n);
 Barrett host_barrett(uint64_t q);
 
+// Blocks are dispatched round-robin over the 8 XCDs of an MI355X: hardware block b runs
+// on XCD b % 8.  xcd_local_block maps b to a logical block so that each XCD works on one
+// contiguous range of logical blocks (and hence of the data), keeping its L2 working set
+// local.  Identity for the tail that does not fill all eight.
+__device__ __forceinline__ uint32_t xcd_local_block(uint32_t b, uint32_t nblocks) {
+  constexpr uint32_t kXcd = 8;
+  const uint32_t full = nblocks - nblocks % kXcd;
+  if (b >= full) return b;
+  return (b % kXcd) * (full / kXcd) + b / kXcd;
+}
+
 // RAII device selection: makes `dev` current and restores the previous device.
 struct DeviceGuard {
   int prev = -1;

@@ -89,17 +89,11 @@ __device__ __forceinline__ int lpos(int pos) {
   return NNTT_LDS_PAD ? pos + (pos >> A::kPadShift) : pos;
 }
 
-// Work placement.  Hardware block b is dispatched to XCD b % 8 of the MI355X.  The
-// logical block lb = xcd_local_block(b) gives each XCD one contiguous range of
-// logical blocks, and logical blocks are ordered limb-major (every batch item and
-// tile of plan limb 0, then limb 1, ...), so an XCD works through a contiguous
-// group of primes and keeps their twiddle tables resident in its own 4 MB L2.
-__device__ __forceinline__ uint32_t xcd_local_block(uint32_t b, uint32_t nblocks) {
-  constexpr uint32_t kXcd = 8;
-  const uint32_t full = nblocks - nblocks % kXcd;
-  if (b >= full) return b;
-  return (b % kXcd) * (full / kXcd) + b / kXcd;
-}
+// Work placement.  The logical block lb = xcd_local_block(b) (internal.h) gives each
+// XCD one contiguous range of logical blocks, and logical blocks are ordered
+// limb-major (every batch item and tile of plan limb 0, then limb 1, ...), so an XCD
+// works through a contiguous group of primes and keeps their twiddle tables resident
+// in its own 4 MB L2.
 struct Place {
   uint64_t row;   // tensor row (batch item * num_limbs + limb)
   uint32_t limb;  // plan limb
