@@ -68,6 +68,23 @@ def test_keyswitch_fused_product_paths(B, logn, bits, nq, npr, dnum):
     assert_bits_equal(host(out), orc.keyswitch(ct, ksk, g, qp, nq, dnum), "keyswitch fused product")
 
 
+@pytest.mark.parametrize("logn,bits,nq,npr,dnum", [(10, 60, 4, 1, 2), (9, 62, 6, 1, 3), (8, 62, 8, 8, 1),
+                                                   (12, 30, 8, 1, 8)])
+def test_keyswitch_degenerate_bases(B, logn, bits, nq, npr, dnum):
+    """One special prime (ModDown's Garner over P is the identity), one-prime digits,
+    a single digit spanning Q, and 30- and 62-bit primes on the whole-limb path."""
+    n = 1 << logn
+    qp = list(primes(bits, 2 * n, nq + npr))
+    plan = B.Plan(n, qp, 0)
+    ks = B.KeySwitchPlan(plan, nq, npr, dnum)
+    ct = residues((2, 2, nq, n), qp[:nq], 9700 + logn + bits)
+    ksk = residues((dnum, 2, nq + npr, n), qp, 9750 + logn + bits)
+    g = 2 * n - 1
+    announce("keyswitch degenerate basis", logn, bits, nq, npr, dnum)
+    out = B.keyswitch(ks, dev(np.zeros_like(ct)), dev(ct), dev(ksk), g)
+    assert_bits_equal(host(out), orc.keyswitch(ct, ksk, g, qp, nq, dnum), "keyswitch degenerate basis")
+
+
 def test_keyswitch_zero_key_and_zero_c1(B):
     n = 1 << 12
     qp, plan, ks = _setup(B, n)
