@@ -1,11 +1,14 @@
-// Element-wise kernels: pointwise products, the ciphertext tensor product and the
-// Galois automorphisms.  All are bound by HBM traffic, so each thread moves 16-byte
-// vectors and the arithmetic (Barrett products) is off the critical path.
+// Element-wise kernels: pointwise products, the ciphertext tensor product, the
+// Galois automorphisms, rescale and the non-canonical count.  All are bound by
+// memory traffic, so each thread moves 16-byte vectors (the coefficient automorphism:
+// one gathered 16-byte pair, two 8-byte stores) and the arithmetic (Barrett and Shoup
+// products) is off the critical path.
 //
 // FHElium ("Eager, Compile, and native execution", section "CUDA execution")
 // maps kernel grids onto the tensor axes limb x coefficient tile x batch; here the
 // [batch][limb][n] tensor is treated as one flat array whose row r has limb
-// r % num_limbs, which covers the same axes with a 1-D grid.
+// r % num_limbs, which covers the same axes with a 1-D grid (split into launches of
+// whole polynomials when it would exceed the launch cap).
 #include <algorithm>
 
 #include "internal.h"
