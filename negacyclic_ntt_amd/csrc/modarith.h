@@ -10,12 +10,26 @@
 // reduction of the 128-bit product (see barrett_mul).
 //
 // CDNA4 issues v_mul_lo_u32 / v_mul_hi_u32 / v_mad_u64_u32 at full rate, so a
-// Shoup product is ~16-19 VALU instructions and a lazy butterfly ~26.
+// Shoup product is ~16 VALU instructions and a lazy butterfly ~24.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace nntt {
+
+// The Shoup remainder y w - Q q, formed mod 2^64 as y w + Q (2^64 - q) from 32-bit
+// halves: the two low products in one multiply-add chain (nothing here waits for the
+// quotient but the second one), the four cross products only into the high word.
+// The empty asm keeps that high word a 32-bit add in place: otherwise the compiler
+// re-forms a 64-bit add of a zero-extended value, one more move and add.
+__device__ __forceinline__ uint64_t shoup_rem(uint32_t y0, uint32_t y1, uint64_t w, uint64_t Q, uint64_t nq) {
+  const uint32_t q0 = (uint32_t)Q, q1 = (uint32_t)(Q >> 32);
+  const uint64_t lo = (uint64_t)q0 * (uint32_t)nq + (uint64_t)y0 * (uint32_t)w;
+  uint32_t hi = y0 * (uint32_t)(w >> 32) + y1 * (uint32_t)w + q0 * (uint32_t)(nq >> 32) + q1 * (uint32_t)nq;
+  hi += (uint32_t)(lo >> 32);
+  asm("" : "+v"(hi));
+  return ((uint64_t)hi << 32) | (uint32_t)lo;
+}
 
 struct Wide {
   using T = uint64_t;
@@ -26,18 +40,10 @@ struct Wide {
   static constexpr bool kSignSelect = false;  // values reach 4q < 2^64: full unsigned compare
   static constexpr int kShoupBits = 64;
 
-  // y * w mod q, result in [0, 2q); any y < 2^64.  Q = hi64(y w'); the remainder
-  // y w - Q q is formed mod 2^64 as y w + Q (2^64 - q): one multiply-add chain
-  // (v_mad_u64_u32 accumulates the two low products) with no borrow to propagate.
+  // y * w mod q, result in [0, 2q); any y < 2^64.  Q = hi64(y w') >= floor(y w / q) - 1.
   static __device__ __forceinline__ T mul(T y, Tw t, T q) {
     const uint64_t Q = __umul64hi(y, t.wp);
-    const uint64_t nq = 0 - q;
-    const uint32_t y0 = (uint32_t)y, y1 = (uint32_t)(y >> 32);
-    const uint32_t q0 = (uint32_t)Q, q1 = (uint32_t)(Q >> 32);
-    const uint64_t lo = (uint64_t)q0 * (uint32_t)nq + (uint64_t)y0 * (uint32_t)t.w;
-    const uint32_t hi = (uint32_t)(lo >> 32) + y0 * (uint32_t)(t.w >> 32) + y1 * (uint32_t)t.w +
-                        q0 * (uint32_t)(nq >> 32) + q1 * (uint32_t)nq;
-    return ((uint64_t)hi << 32) | (uint32_t)lo;
+    return shoup_rem((uint32_t)y, (uint32_t)(y >> 32), t.w, Q, 0 - q);
   }
   static __device__ __forceinline__ T load(const uint64_t* p) { return *p; }
   static __device__ __forceinline__ uint64_t widen(T x) { return x; }
@@ -62,16 +68,15 @@ struct Wide60 {
   static __device__ __forceinline__ T mul(T y, Tw t, T q) {
     const uint32_t y0 = (uint32_t)y, y1 = (uint32_t)(y >> 32);
     const uint32_t p0 = (uint32_t)t.wp, p1 = (uint32_t)(t.wp >> 32);
-    uint64_t S = (uint64_t)y0 * p1 + __umulhi(y0, p0);
-    S = (uint64_t)y1 * p0 + S;
-    const uint64_t H = (uint64_t)y1 * p1 + (S >> 32);
-    const uint64_t Q = (H << 2) | ((uint32_t)S >> 30);
-    const uint64_t nq = 0 - q;
-    const uint32_t q0 = (uint32_t)Q, q1 = (uint32_t)(Q >> 32);
-    const uint64_t lo = (uint64_t)q0 * (uint32_t)nq + (uint64_t)y0 * (uint32_t)t.w;
-    const uint32_t hi = (uint32_t)(lo >> 32) + y0 * (uint32_t)(t.w >> 32) + y1 * (uint32_t)t.w + q0 * (uint32_t)(nq >> 32) +
-                        q1 * (uint32_t)nq;
-    return ((uint64_t)hi << 32) | (uint32_t)lo;
+    uint64_t S = (uint64_t)y1 * p0 + __umulhi(y0, p0);
+    S = (uint64_t)y0 * p1 + S;
+    // (y1 p1 2^32 + S) >> 30 = 4 y1 p1 + (S >> 30): one 64-bit shift and one
+    // shift-add.  The empty asm keeps the product whole; otherwise the shift by 2 is
+    // folded into p1 and the product splits in two.
+    uint64_t P11 = (uint64_t)y1 * p1;
+    asm("" : "+v"(P11));
+    const uint64_t Q = (P11 << 2) + (S >> 30);
+    return shoup_rem(y0, y1, t.w, Q, 0 - q);
   }
   static __device__ __forceinline__ uint64_t widen(T x) { return x; }
 };
