@@ -89,6 +89,9 @@ def parse():
     ap.add_argument("--no-next-rows", action="store_true", help="skip relin / rescale / hoisted / modraise timings")
     ap.add_argument("--no-other-configs", action="store_true", help="skip the n = 2^14 and n = 2048 workloads")
     ap.add_argument("--next-reps", type=int, default=10)
+    ap.add_argument("--sustained", type=int, default=0, metavar="K",
+                    help="instead of the step: K forward transforms of the large-ring batch back to back, "
+                         "each timed with HIP events (shows the clock falling under sustained load)")
     ap.add_argument("--cpu-sample-limbs", type=int, default=384,
                     help="limbs of the batch the oracle processes for the CPU baseline (384 = all 16 polys)")
     return ap.parse_args()
@@ -324,6 +327,30 @@ def device_info():
     return info
 
 
+def sustained(B, calls):
+    """K back-to-back forward transforms of the large-ring batch over four resident copies.
+    Events between calls add no gaps; one JSON line with every call's duration."""
+    import torch
+    from negacyclic_ntt_amd import inputs, workloads
+    W = workloads.RING
+    primes = B.find_primes(W.bits, W.n, W.limbs)
+    plan = B.Plan(W.n, primes, 0)
+    a0 = B.to_device(inputs.uniform_residues(W.shape_a, primes, W.seed_a))
+    sets = [a0] + [a0.clone() for _ in range(3)]
+    B.ntt_forward(plan, sets[3])  # loads the kernels; untimed
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(calls + 1)]
+    ev[0].record()
+    for i in range(calls):
+        B.ntt_forward(plan, sets[i % 4])
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    us = [round(ev[i].elapsed_time(ev[i + 1]) * 1e3, 1) for i in range(calls)]
+    head, tail = us[: min(8, calls)], us[-min(10, calls):]
+    return {"mode": "sustained_ntt_forward", "workload": W.name, "calls": calls, "us_per_call": us,
+            "first_calls_mean_us": round(sum(head) / len(head), 1), "last_calls_mean_us": round(sum(tail) / len(tail), 1)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -338,6 +365,9 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
+    if args.sustained > 0:
+        print(json.dumps(sustained(B, args.sustained)), flush=True)
+        return
     dev = torch.device("cuda:0")
     W, KS = workloads.RING, workloads.KEYSWITCH
     n, L, nq, npr, dnum = W.n, W.limbs, KS.limbs, KS.special, KS.dnum
