@@ -71,7 +71,7 @@ constexpr Sched make_sched(int logm) {
 #define NNTT_ROW_FWD_PRELOAD 0
 #endif
 #ifndef NNTT_COL_TW_LDS
-#define NNTT_COL_TW_LDS 1  // measured on MI355X: forward 2^16 NTT 2.5% faster
+#define NNTT_COL_TW_LDS 0  // MI355X: staging in LDS ties in the bench step, 4-5% slower back to back
 #endif
 #ifndef NNTT_LDS_PAD
 #define NNTT_LDS_PAD 1
