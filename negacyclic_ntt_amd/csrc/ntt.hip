@@ -243,8 +243,8 @@ __device__ __forceinline__ uint64_t finish(typename A::T x, const ModInfo& m) {
   using T = typename A::T;
   const T q = (T)m.q;
   if (FWD) {
-    x = csub<T>(x, q + q);
-    return A::widen(csub<T>(x, q));
+    x = reduce_once<A>(x, q + q);
+    return A::widen(reduce_once<A>(x, q));
   }
   typename A::Tw s;
   if constexpr (A::kShoupBits == 64) {
@@ -257,7 +257,7 @@ __device__ __forceinline__ uint64_t finish(typename A::T x, const ModInfo& m) {
     s.w = m.n_inv32;
     s.wp = m.n_inv_shoup32;
   }
-  return A::widen(csub<T>(A::mul(x, s, q), q));
+  return A::widen(reduce_once<A>(A::mul(x, s, q), q));
 }
 
 // ---------------------------------------------------------------------------
