@@ -17,6 +17,10 @@ struct ModInfo {
   uint64_t n_inv, n_inv_shoup;  // n^-1 mod q and floor(n^-1 * 2^64 / q)
   uint64_t n_inv_shoup60;       // floor(n^-1 * 2^62 / q) (primes below 2^60)
   uint32_t n_inv32, n_inv_shoup32;  // narrow (q < 2^30) Shoup pair, else 0
+  // w1n = psi^-brv(1) n^-1 mod q: the inverse network's last-stage twiddle with the
+  // final scaling folded in, and its Shoup companions (2^64, 2^62, 2^32 scaled).
+  uint64_t w1n, w1n_shoup, w1n_shoup60;
+  uint32_t w1n32, w1n_shoup32;
   Barrett br;
   uint64_t mont_ninv;  // -q^-1 mod 2^64 (Montgomery reduction with R = 2^64)
   uint64_t r64, r64_shoup;  // 2^64 mod q and floor(r64 2^64 / q): undoes a Montgomery reduction

@@ -150,6 +150,18 @@ __device__ __forceinline__ void gs_butterfly(typename A::T& x, typename A::T& y,
   y = A::mul(d, w, q);
 }
 
+// The inverse network's last stage with the final n^-1 folded in: (x + y) n^-1 and
+// (x - y) w n^-1, each one Shoup product.  In: x, y in [0, 2q).  Out: both in [0, 2q).
+template <class A>
+__device__ __forceinline__ void gs_butterfly_scaled(typename A::T& x, typename A::T& y, typename A::Tw ninv,
+                                                    typename A::Tw wn, typename A::T q, typename A::T two_q) {
+  using T = typename A::T;
+  const T s = x + y;
+  const T d = x - y + two_q;
+  x = A::mul(s, ninv, q);
+  y = A::mul(d, wn, q);
+}
+
 // Barrett reduction of a full product of two canonical 64-bit residues.
 // q < 2^62 with k = bitlen(q); mu = floor(2^(2k) / q) < 2^63.
 // q1 = floor(x / 2^(k-1)), q3 = floor(q1 * mu / 2^(k+1)); then

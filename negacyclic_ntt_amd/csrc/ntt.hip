@@ -76,6 +76,9 @@ constexpr Sched make_sched(int logm) {
 #ifndef NNTT_LDS_PAD
 #define NNTT_LDS_PAD 1
 #endif
+#ifndef NNTT_INV_FOLD
+#define NNTT_INV_FOLD 1  // the column pass of the inverse folds n^-1 into its last stage
+#endif
 #ifndef NNTT_SPLIT_MIN_LOGN
 #define NNTT_SPLIT_MIN_LOGN 15  // smallest ring that uses the two-pass split
 #endif
@@ -117,15 +120,19 @@ struct SubParams {
   const typename A::Tw* tw;  // this prime's table (n entries)
   typename A::T q;
   uint32_t prefix;
+  typename A::Tw ninv, w1n;  // last inverse stage with the scaling folded in (FOLD only)
 };
 
 // One pass: radix 2^R sets over stages [S0, S0 + R) of every sub-transform held
 // in LDS.  NSUB sub-transforms of size 2^LOGM, NT threads.
 // PRE: 1 requests every twiddle of a set before its LDS reads, 0 loads them as the
 // butterflies need them, -1 takes the direction's default (forward 0, inverse 1).
-template <class A, bool FWD, int LOGM, int R, int S0, int NSUB, int NT, int PRE, class GetSub>
+// FOLD (inverse, S0 = 0): stage 0 is the transform's last one, prefix 1, and scales by
+// n^-1 as it goes (gs_butterfly_scaled with sp.ninv and sp.w1n).
+template <class A, bool FWD, int LOGM, int R, int S0, int NSUB, int NT, int PRE, class GetSub, bool FOLD = false>
 __device__ __forceinline__ void run_pass(typename A::T* lds, int tid, const GetSub& get_sub) {
   using T = typename A::T;
+  static_assert(!FOLD || (!FWD && S0 == 0), "the folded scaling belongs to the inverse's stage 0");
   constexpr int M = 1 << LOGM;
   constexpr int SETS_PER_SUB = M >> R;
   constexpr int TP = M >> (S0 + R);  // smallest distance in this pass
@@ -184,7 +191,10 @@ __device__ __forceinline__ void run_pass(typename A::T* lds, int tid, const GetS
 #pragma unroll
         for (int i = 0; i < (1 << R); ++i) {
           if (i & half) continue;
-          gs_butterfly<A>(x[i], x[i + half], sp.tw[(pg << v) + (uint32_t)(i >> (R - v))], q, two_q);
+          if (FOLD && v == 0)
+            gs_butterfly_scaled<A>(x[i], x[i + half], sp.ninv, sp.w1n, q, two_q);
+          else
+            gs_butterfly<A>(x[i], x[i + half], sp.tw[(pg << v) + (uint32_t)(i >> (R - v))], q, two_q);
         }
       }
     } else {
@@ -205,7 +215,10 @@ __device__ __forceinline__ void run_pass(typename A::T* lds, int tid, const GetS
 #pragma unroll
         for (int i = 0; i < (1 << R); ++i) {
           if (i & half) continue;
-          gs_butterfly<A>(x[i], x[i + half], wv[(1 << v) - 1 + (i >> (R - v))], q, two_q);
+          if (FOLD && v == 0)
+            gs_butterfly_scaled<A>(x[i], x[i + half], sp.ninv, sp.w1n, q, two_q);
+          else
+            gs_butterfly<A>(x[i], x[i + half], wv[(1 << v) - 1 + (i >> (R - v))], q, two_q);
         }
       }
     }
@@ -216,14 +229,15 @@ __device__ __forceinline__ void run_pass(typename A::T* lds, int tid, const GetS
 
 // All passes of a sub-transform of size 2^LOGM, forward (sigma up) or inverse
 // (sigma down).  Ends with a barrier.
-template <class A, bool FWD, int LOGM, int NSUB, int NT, int P, class GetSub, int PRE = -1>
+// FOLD (inverse only): the last pass scales by n^-1 (see run_pass).
+template <class A, bool FWD, int LOGM, int NSUB, int NT, int P, class GetSub, int PRE = -1, bool FOLD = false>
 __device__ __forceinline__ void run_passes(typename A::T* lds, int tid, const GetSub& get_sub) {
   constexpr Sched S = make_sched(LOGM);
   if constexpr (P < S.np) {
     constexpr int idx = FWD ? P : S.np - 1 - P;
-    run_pass<A, FWD, LOGM, S.r[idx], S.s[idx], NSUB, NT, PRE>(lds, tid, get_sub);
+    run_pass<A, FWD, LOGM, S.r[idx], S.s[idx], NSUB, NT, PRE, GetSub, FOLD && P == S.np - 1>(lds, tid, get_sub);
     __syncthreads();
-    run_passes<A, FWD, LOGM, NSUB, NT, P + 1, GetSub, PRE>(lds, tid, get_sub);
+    run_passes<A, FWD, LOGM, NSUB, NT, P + 1, GetSub, PRE, FOLD>(lds, tid, get_sub);
   }
 }
 
@@ -238,10 +252,12 @@ __device__ __forceinline__ typename A::T modulus(const ModInfo& m) {
 }
 
 // Final store conversion: forward [0, 4q) -> [0, q); inverse: * n^-1 then [0, q).
-template <class A, bool FWD>
+// SCALED (inverse): the last stage already multiplied by n^-1; x in [0, 2q).
+template <class A, bool FWD, bool SCALED = false>
 __device__ __forceinline__ uint64_t finish(typename A::T x, const ModInfo& m) {
   using T = typename A::T;
   const T q = (T)m.q;
+  if constexpr (SCALED) return A::widen(reduce_once<A>(x, q));
   if (FWD) {
     x = reduce_once<A>(x, q + q);
     return A::widen(reduce_once<A>(x, q));
@@ -258,6 +274,21 @@ __device__ __forceinline__ uint64_t finish(typename A::T x, const ModInfo& m) {
     s.wp = m.n_inv_shoup32;
   }
   return A::widen(reduce_once<A>(A::mul(x, s, q), q));
+}
+
+// n^-1 and psi^-brv(1) n^-1 as Shoup pairs of the residue width.
+template <class A>
+__device__ __forceinline__ void scaled_last_stage(const ModInfo& m, typename A::Tw& ninv, typename A::Tw& w1n) {
+  if constexpr (A::kShoupBits == 64) {
+    ninv.w = m.n_inv, ninv.wp = m.n_inv_shoup;
+    w1n.w = m.w1n, w1n.wp = m.w1n_shoup;
+  } else if constexpr (A::kShoupBits == 62) {
+    ninv.w = m.n_inv, ninv.wp = m.n_inv_shoup60;
+    w1n.w = m.w1n, w1n.wp = m.w1n_shoup60;
+  } else {
+    ninv.w = m.n_inv32, ninv.wp = m.n_inv_shoup32;
+    w1n.w = m.w1n32, w1n.wp = m.w1n_shoup32;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -336,7 +367,8 @@ __global__ __launch_bounds__(LdsCfg<LOGN>::NT) void ntt_lds_kernel(uint64_t* dat
     return sp;
   };
   // Inverse: twiddles on demand (measured on MI355X: n = 2^14, 2048 limbs, 307 -> 291 us;
-  // the same at n = 2048).
+  // the same at n = 2048).  The n^-1 scaling stays in the store: folded into the last
+  // stage as in the column pass it was 1% slower at n = 2^14.
   run_passes<A, FWD, LOGN, ROWS, NT, 0, decltype(get_sub), 0>(lds, tid, get_sub);
 
   static_assert((ROWS * N) % (2 * NT) == 0, "whole iterations");
@@ -465,8 +497,11 @@ __global__ __launch_bounds__(ColCfg<LOGN1>::NT) void ntt_col_kernel(uint64_t* da
 #endif
   sp.q = modulus<A>(m);
   sp.prefix = 1;
+  // The inverse's last launch folds n^-1 into its last stage.
+  constexpr bool kFold = !FWD && LAST && NNTT_INV_FOLD;
+  if constexpr (kFold) scaled_last_stage<A>(m, sp.ninv, sp.w1n);
   auto get_sub = [&](int) { return sp; };
-  run_passes<A, FWD, LOGN1, kCols, NT, 0>(lds, tid, get_sub);
+  run_passes<A, FWD, LOGN1, kCols, NT, 0, decltype(get_sub), -1, kFold>(lds, tid, get_sub);
 
   static_assert((kCols * N1) % (2 * NT) == 0, "whole iterations");
 #pragma unroll
@@ -475,8 +510,8 @@ __global__ __launch_bounds__(ColCfg<LOGN1>::NT) void ntt_col_kernel(uint64_t* da
     const int rr = e / kCols, c = e % kCols;
     ulonglong2 v;
     if (LAST) {
-      v.x = finish<A, FWD>(lds[c * STRIDE + lpos<A>(rr)], m);
-      v.y = finish<A, FWD>(lds[(c + 1) * STRIDE + lpos<A>(rr)], m);
+      v.x = finish<A, FWD, kFold>(lds[c * STRIDE + lpos<A>(rr)], m);
+      v.y = finish<A, FWD, kFold>(lds[(c + 1) * STRIDE + lpos<A>(rr)], m);
     } else {
       v.x = A::widen(lds[c * STRIDE + lpos<A>(rr)]);
       v.y = A::widen(lds[(c + 1) * STRIDE + lpos<A>(rr)]);

@@ -285,6 +285,13 @@ extern "C" int ntt_plan_create(ntt_plan** out, uint32_t n, const uint64_t* prime
       m.n_inv32 = (uint32_t)m.n_inv;
       m.n_inv_shoup32 = (uint32_t)(((uint64_t)m.n_inv << 32) / q);
     }
+    m.w1n = host_mulmod(p->h_inv[(size_t)l * n + 1], m.n_inv, q);
+    m.w1n_shoup = (uint64_t)(((u128)m.w1n << 64) / q);
+    m.w1n_shoup60 = p->below60[l] ? (uint64_t)(((u128)m.w1n << 62) / q) : 0;
+    if (p->narrow[l]) {
+      m.w1n32 = (uint32_t)m.w1n;
+      m.w1n_shoup32 = (uint32_t)(((uint64_t)m.w1n << 32) / q);
+    }
     m.br = host_barrett(q);
     uint64_t inv = q;  // Newton: q * q == 1 mod 8, each step doubles the correct bits
     for (int it = 0; it < 5; ++it) inv *= 2 - q * inv;
