@@ -128,11 +128,12 @@ __device__ __forceinline__ typename A::T reduce_once(typename A::T x, typename A
 
 // Cooley-Tukey (decimation in time) butterfly with lazy reduction.
 // In: x, y in [0, 4q).  Out: x + w y, x - w y + 2q, both in [0, 4q).
-template <class A>
+// CANON: x is canonical (< q), as on a transform's first stage: no reduction.
+template <class A, bool CANON = false>
 __device__ __forceinline__ void ct_butterfly(typename A::T& x, typename A::T& y, typename A::Tw w, typename A::T q,
                                              typename A::T two_q) {
   using T = typename A::T;
-  T u = reduce_once<A>(x, two_q);
+  T u = CANON ? x : reduce_once<A>(x, two_q);
   T t = A::mul(y, w, q);
   x = u + t;
   y = u - t + two_q;
@@ -140,13 +141,14 @@ __device__ __forceinline__ void ct_butterfly(typename A::T& x, typename A::T& y,
 
 // Gentleman-Sande (decimation in frequency) butterfly with lazy reduction.
 // In: x, y in [0, 2q).  Out: x + y, (x - y) w, both in [0, 2q).
-template <class A>
+// CANON: x, y canonical (< q), as on a transform's first stage: x + y < 2q as it is.
+template <class A, bool CANON = false>
 __device__ __forceinline__ void gs_butterfly(typename A::T& x, typename A::T& y, typename A::Tw w, typename A::T q,
                                              typename A::T two_q) {
   using T = typename A::T;
   T s = x + y;
   T d = x - y + two_q;
-  x = reduce_once<A>(s, two_q);
+  x = CANON ? s : reduce_once<A>(s, two_q);
   y = A::mul(d, w, q);
 }
 

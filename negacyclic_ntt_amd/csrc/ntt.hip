@@ -79,6 +79,9 @@ constexpr Sched make_sched(int logm) {
 #ifndef NNTT_INV_FOLD
 #define NNTT_INV_FOLD 1  // the column pass of the inverse folds n^-1 into its last stage
 #endif
+#ifndef NNTT_CANON_FIRST
+#define NNTT_CANON_FIRST 1  // a transform's first stage takes canonical inputs unreduced
+#endif
 #ifndef NNTT_SPLIT_MIN_LOGN
 #define NNTT_SPLIT_MIN_LOGN 15  // smallest ring that uses the two-pass split
 #endif
@@ -129,7 +132,10 @@ struct SubParams {
 // butterflies need them, -1 takes the direction's default (forward 0, inverse 1).
 // FOLD (inverse, S0 = 0): stage 0 is the transform's last one, prefix 1, and scales by
 // n^-1 as it goes (gs_butterfly_scaled with sp.ninv and sp.w1n).
-template <class A, bool FWD, int LOGM, int R, int S0, int NSUB, int NT, int PRE, class GetSub, bool FOLD = false>
+// CANON: the pass starts the transform on canonical inputs, so its first stage skips
+// the butterflies' input reduction.
+template <class A, bool FWD, int LOGM, int R, int S0, int NSUB, int NT, int PRE, class GetSub, bool FOLD = false,
+          bool CANON = false>
 __device__ __forceinline__ void run_pass(typename A::T* lds, int tid, const GetSub& get_sub) {
   using T = typename A::T;
   static_assert(!FOLD || (!FWD && S0 == 0), "the folded scaling belongs to the inverse's stage 0");
@@ -166,7 +172,10 @@ __device__ __forceinline__ void run_pass(typename A::T* lds, int tid, const GetS
 #pragma unroll
         for (int i = 0; i < (1 << R); ++i) {
           if (i & half) continue;
-          ct_butterfly<A>(x[i], x[i + half], wv[(1 << v) - 1 + (i >> (R - v))], q, two_q);
+          if (CANON && v == 0)
+            ct_butterfly<A, true>(x[i], x[i + half], wv[(1 << v) - 1 + (i >> (R - v))], q, two_q);
+          else
+            ct_butterfly<A>(x[i], x[i + half], wv[(1 << v) - 1 + (i >> (R - v))], q, two_q);
         }
       }
     } else if (FWD) {
@@ -179,7 +188,10 @@ __device__ __forceinline__ void run_pass(typename A::T* lds, int tid, const GetS
         for (int i = 0; i < (1 << R); ++i) {
           if (i & half) continue;
           const typename A::Tw w = sp.tw[(pg << v) + (uint32_t)(i >> (R - v))];
-          ct_butterfly<A>(x[i], x[i + half], w, q, two_q);
+          if (CANON && v == 0)
+            ct_butterfly<A, true>(x[i], x[i + half], w, q, two_q);
+          else
+            ct_butterfly<A>(x[i], x[i + half], w, q, two_q);
         }
       }
     } else if (PRE == 0) {
@@ -193,6 +205,8 @@ __device__ __forceinline__ void run_pass(typename A::T* lds, int tid, const GetS
           if (i & half) continue;
           if (FOLD && v == 0)
             gs_butterfly_scaled<A>(x[i], x[i + half], sp.ninv, sp.w1n, q, two_q);
+          else if (CANON && v == R - 1)
+            gs_butterfly<A, true>(x[i], x[i + half], sp.tw[(pg << v) + (uint32_t)(i >> (R - v))], q, two_q);
           else
             gs_butterfly<A>(x[i], x[i + half], sp.tw[(pg << v) + (uint32_t)(i >> (R - v))], q, two_q);
         }
@@ -217,6 +231,8 @@ __device__ __forceinline__ void run_pass(typename A::T* lds, int tid, const GetS
           if (i & half) continue;
           if (FOLD && v == 0)
             gs_butterfly_scaled<A>(x[i], x[i + half], sp.ninv, sp.w1n, q, two_q);
+          else if (CANON && v == R - 1)
+            gs_butterfly<A, true>(x[i], x[i + half], wv[(1 << v) - 1 + (i >> (R - v))], q, two_q);
           else
             gs_butterfly<A>(x[i], x[i + half], wv[(1 << v) - 1 + (i >> (R - v))], q, two_q);
         }
@@ -229,15 +245,18 @@ __device__ __forceinline__ void run_pass(typename A::T* lds, int tid, const GetS
 
 // All passes of a sub-transform of size 2^LOGM, forward (sigma up) or inverse
 // (sigma down).  Ends with a barrier.
-// FOLD (inverse only): the last pass scales by n^-1 (see run_pass).
-template <class A, bool FWD, int LOGM, int NSUB, int NT, int P, class GetSub, int PRE = -1, bool FOLD = false>
+// FOLD (inverse only): the last pass scales by n^-1 (see run_pass).  CANON: these
+// passes start the transform on canonical inputs (see run_pass).
+template <class A, bool FWD, int LOGM, int NSUB, int NT, int P, class GetSub, int PRE = -1, bool FOLD = false,
+          bool CANON = false>
 __device__ __forceinline__ void run_passes(typename A::T* lds, int tid, const GetSub& get_sub) {
   constexpr Sched S = make_sched(LOGM);
   if constexpr (P < S.np) {
     constexpr int idx = FWD ? P : S.np - 1 - P;
-    run_pass<A, FWD, LOGM, S.r[idx], S.s[idx], NSUB, NT, PRE, GetSub, FOLD && P == S.np - 1>(lds, tid, get_sub);
+    run_pass<A, FWD, LOGM, S.r[idx], S.s[idx], NSUB, NT, PRE, GetSub, FOLD && P == S.np - 1, CANON && P == 0>(
+        lds, tid, get_sub);
     __syncthreads();
-    run_passes<A, FWD, LOGM, NSUB, NT, P + 1, GetSub, PRE, FOLD>(lds, tid, get_sub);
+    run_passes<A, FWD, LOGM, NSUB, NT, P + 1, GetSub, PRE, FOLD, CANON>(lds, tid, get_sub);
   }
 }
 
@@ -369,7 +388,7 @@ __global__ __launch_bounds__(LdsCfg<LOGN>::NT) void ntt_lds_kernel(uint64_t* dat
   // Inverse: twiddles on demand (measured on MI355X: n = 2^14, 2048 limbs, 307 -> 291 us;
   // the same at n = 2048).  The n^-1 scaling stays in the store: folded into the last
   // stage as in the column pass it was 1% slower at n = 2^14.
-  run_passes<A, FWD, LOGN, ROWS, NT, 0, decltype(get_sub), 0>(lds, tid, get_sub);
+  run_passes<A, FWD, LOGN, ROWS, NT, 0, decltype(get_sub), 0, false, NNTT_CANON_FIRST>(lds, tid, get_sub);
 
   static_assert((ROWS * N) % (2 * NT) == 0, "whole iterations");
 #pragma unroll
@@ -501,7 +520,7 @@ __global__ __launch_bounds__(ColCfg<LOGN1>::NT) void ntt_col_kernel(uint64_t* da
   constexpr bool kFold = !FWD && LAST && NNTT_INV_FOLD;
   if constexpr (kFold) scaled_last_stage<A>(m, sp.ninv, sp.w1n);
   auto get_sub = [&](int) { return sp; };
-  run_passes<A, FWD, LOGN1, kCols, NT, 0, decltype(get_sub), -1, kFold>(lds, tid, get_sub);
+  run_passes<A, FWD, LOGN1, kCols, NT, 0, decltype(get_sub), -1, kFold, FWD && NNTT_CANON_FIRST>(lds, tid, get_sub);
 
   static_assert((kCols * N1) % (2 * NT) == 0, "whole iterations");
 #pragma unroll
@@ -566,7 +585,8 @@ __global__ __launch_bounds__(RowCfg<LOGN2>::NT) void ntt_row_kernel(uint64_t* __
     sp.prefix = (uint32_t)N1 + (GAL ? galois_row<LOGN1>((uint32_t)(r0 + sub), galois) : (uint32_t)(r0 + sub));
     return sp;
   };
-  run_passes<A, FWD, LOGN2, kRows, NT, 0, decltype(get_sub), NNTT_ROW_FWD_PRELOAD ? 1 : -1>(lds, tid, get_sub);
+  run_passes<A, FWD, LOGN2, kRows, NT, 0, decltype(get_sub), NNTT_ROW_FWD_PRELOAD ? 1 : -1, false,
+             !FWD && NNTT_CANON_FIRST>(lds, tid, get_sub);
 
   static_assert((kRows * N2) % (2 * NT) == 0, "whole iterations");
 #pragma unroll
@@ -686,7 +706,7 @@ __global__ __launch_bounds__(RowCfg<LOGN2>::NT) void ntt_row_mac_kernel(uint64_t
     sp.prefix = (uint32_t)N1 + (uint32_t)(pl.tile * kRows + sub);
     return sp;
   };
-  run_passes<A, false, LOGN2, kRows, NT, 0>(lds, tid, get_sub);
+  run_passes<A, false, LOGN2, kRows, NT, 0, decltype(get_sub), -1, false, NNTT_CANON_FIRST>(lds, tid, get_sub);
 
   uint64_t* base = acc + row * N + off;
   static_assert((kRows * N2) % (2 * NT) == 0, "whole iterations");
@@ -782,7 +802,7 @@ __global__ __launch_bounds__(RowCfg<LOGN2>::NT) void ntt_row_mac_hoisted_kernel(
     sp.prefix = (uint32_t)N1 + (uint32_t)(pl.tile * kRows + sub);
     return sp;
   };
-  run_passes<A, false, LOGN2, kRows, NT, 0>(lds, tid, get_sub);
+  run_passes<A, false, LOGN2, kRows, NT, 0, decltype(get_sub), -1, false, NNTT_CANON_FIRST>(lds, tid, get_sub);
 
   uint64_t* base = acc + row * N + off;
 #pragma unroll
