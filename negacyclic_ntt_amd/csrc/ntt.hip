@@ -68,7 +68,10 @@ constexpr Sched make_sched(int logm) {
 }
 
 #ifndef NNTT_ROW_FWD_PRELOAD
-#define NNTT_ROW_FWD_PRELOAD 0
+#define NNTT_ROW_FWD_PRELOAD 1  // MI355X: bench step +1.4%, forward -2%, key-switch -2.6%
+#endif
+#ifndef NNTT_COL_FWD_PRELOAD
+#define NNTT_COL_FWD_PRELOAD 1  // MI355X: forward -0.7% in the bench step, -1.6% back to back
 #endif
 #ifndef NNTT_COL_TW_LDS
 #define NNTT_COL_TW_LDS 0  // MI355X: staging in LDS ties in the bench step, 4-5% slower back to back
@@ -520,7 +523,8 @@ __global__ __launch_bounds__(ColCfg<LOGN1>::NT) void ntt_col_kernel(uint64_t* da
   constexpr bool kFold = !FWD && LAST && NNTT_INV_FOLD;
   if constexpr (kFold) scaled_last_stage<A>(m, sp.ninv, sp.w1n);
   auto get_sub = [&](int) { return sp; };
-  run_passes<A, FWD, LOGN1, kCols, NT, 0, decltype(get_sub), -1, kFold, FWD && NNTT_CANON_FIRST>(lds, tid, get_sub);
+  run_passes<A, FWD, LOGN1, kCols, NT, 0, decltype(get_sub), NNTT_COL_FWD_PRELOAD ? 1 : -1, kFold,
+             FWD && NNTT_CANON_FIRST>(lds, tid, get_sub);
 
   static_assert((kCols * N1) % (2 * NT) == 0, "whole iterations");
 #pragma unroll
