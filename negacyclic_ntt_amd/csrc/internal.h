@@ -37,6 +37,19 @@ __host__ __device__ inline size_t rescale_index(uint32_t k, uint32_t l) { return
 
 constexpr uint32_t kMaxLogN = 16;
 
+// Device twiddle layout for the two-pass split (n = 2^15, 2^16: rows of N2 = 2^8, the
+// row transform in two radix-16 passes).  The row transform's last pass (row stages
+// 4..7) reads, for row r and set u (0..15) at row stage 4 + v, the 2^v entries
+// ((N1 + r) 2^4 + u) 2^v + j.  Stored instead at (N1 + r) 2^(4 + v) + j 2^4 + u, so that
+// for each (v, j) the 16 sets of a row read 16 consecutive entries: each stage block
+// [2^s, 2^(s+1)) is permuted within each row's sub-block only.  Host copies returned
+// by ntt_plan_get_tables keep the plain order.
+#ifndef NNTT_ROW_TW_PERM
+#define NNTT_ROW_TW_PERM 1
+#endif
+constexpr uint32_t kPermMinLogN = 15, kPermRowLog = 8, kPermRowS0 = 4;
+__host__ __device__ constexpr bool row_tw_permuted(uint32_t logn) { return NNTT_ROW_TW_PERM && logn >= kPermMinLogN; }
+
 // The NTT-domain automorphism in bit-reversed slot order: out[k] = in[slot(k)] with
 // 2 brv(slot) + 1 = (2 brv(k) + 1) g mod 2n, i.e. brv(slot) = g brv(k) + (g - 1) / 2
 // mod n.  It maps every aligned segment of 2^m slots onto an aligned segment: the

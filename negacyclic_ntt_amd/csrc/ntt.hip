@@ -137,8 +137,10 @@ struct SubParams {
 // n^-1 as it goes (gs_butterfly_scaled with sp.ninv and sp.w1n).
 // CANON: the pass starts the transform on canonical inputs, so its first stage skips
 // the butterflies' input reduction.
+// PERM: the table is in the row-pass layout (internal.h): stage v, entry j of set g is
+// at (prefix 2^S0) 2^v + j 2^S0 + g instead of (prefix 2^S0 + g) 2^v + j.
 template <class A, bool FWD, int LOGM, int R, int S0, int NSUB, int NT, int PRE, class GetSub, bool FOLD = false,
-          bool CANON = false>
+          bool CANON = false, bool PERM = false>
 __device__ __forceinline__ void run_pass(typename A::T* lds, int tid, const GetSub& get_sub) {
   using T = typename A::T;
   static_assert(!FOLD || (!FWD && S0 == 0), "the folded scaling belongs to the inverse's stage 0");
@@ -159,6 +161,10 @@ __device__ __forceinline__ void run_pass(typename A::T* lds, int tid, const GetS
     const SubParams<A> sp = get_sub(sub);
     const T q = sp.q, two_q = q + q;
     const uint32_t pg = (sp.prefix << S0) + (uint32_t)g;
+    // Table index of stage v, entry j of this set.
+    auto twi = [&](int v, uint32_t j) -> uint32_t {
+      return PERM ? ((sp.prefix << S0) << v) + (j << S0) + (uint32_t)g : (pg << v) + j;
+    };
     T x[1 << R];
     if (FWD && PRE == 1) {
       // Forward with every twiddle of the set requested before the LDS reads.
@@ -166,7 +172,7 @@ __device__ __forceinline__ void run_pass(typename A::T* lds, int tid, const GetS
 #pragma unroll
       for (int v = 0; v < R; ++v)
 #pragma unroll
-        for (int j = 0; j < (1 << v); ++j) wv[(1 << v) - 1 + j] = sp.tw[(pg << v) + (uint32_t)j];
+        for (int j = 0; j < (1 << v); ++j) wv[(1 << v) - 1 + j] = sp.tw[twi(v, (uint32_t)j)];
 #pragma unroll
       for (int i = 0; i < (1 << R); ++i) x[i] = base[lpos<A>(pos0 + i * TP)];
 #pragma unroll
@@ -190,7 +196,7 @@ __device__ __forceinline__ void run_pass(typename A::T* lds, int tid, const GetS
 #pragma unroll
         for (int i = 0; i < (1 << R); ++i) {
           if (i & half) continue;
-          const typename A::Tw w = sp.tw[(pg << v) + (uint32_t)(i >> (R - v))];
+          const typename A::Tw w = sp.tw[twi(v, (uint32_t)(i >> (R - v)))];
           if (CANON && v == 0)
             ct_butterfly<A, true>(x[i], x[i + half], w, q, two_q);
           else
@@ -209,9 +215,9 @@ __device__ __forceinline__ void run_pass(typename A::T* lds, int tid, const GetS
           if (FOLD && v == 0)
             gs_butterfly_scaled<A>(x[i], x[i + half], sp.ninv, sp.w1n, q, two_q);
           else if (CANON && v == R - 1)
-            gs_butterfly<A, true>(x[i], x[i + half], sp.tw[(pg << v) + (uint32_t)(i >> (R - v))], q, two_q);
+            gs_butterfly<A, true>(x[i], x[i + half], sp.tw[twi(v, (uint32_t)(i >> (R - v)))], q, two_q);
           else
-            gs_butterfly<A>(x[i], x[i + half], sp.tw[(pg << v) + (uint32_t)(i >> (R - v))], q, two_q);
+            gs_butterfly<A>(x[i], x[i + half], sp.tw[twi(v, (uint32_t)(i >> (R - v)))], q, two_q);
         }
       }
     } else {
@@ -223,7 +229,7 @@ __device__ __forceinline__ void run_pass(typename A::T* lds, int tid, const GetS
 #pragma unroll
       for (int v = 0; v < R; ++v)
 #pragma unroll
-        for (int j = 0; j < (1 << v); ++j) wv[(1 << v) - 1 + j] = sp.tw[(pg << v) + (uint32_t)j];
+        for (int j = 0; j < (1 << v); ++j) wv[(1 << v) - 1 + j] = sp.tw[twi(v, (uint32_t)j)];
 #pragma unroll
       for (int i = 0; i < (1 << R); ++i) x[i] = base[lpos<A>(pos0 + i * TP)];
 #pragma unroll
@@ -250,16 +256,20 @@ __device__ __forceinline__ void run_pass(typename A::T* lds, int tid, const GetS
 // (sigma down).  Ends with a barrier.
 // FOLD (inverse only): the last pass scales by n^-1 (see run_pass).  CANON: these
 // passes start the transform on canonical inputs (see run_pass).
+// ROWT: the row transform of the two-pass split reading the row-pass table layout
+// (its last pass, row stages kPermRowS0.., uses PERM indexing).
 template <class A, bool FWD, int LOGM, int NSUB, int NT, int P, class GetSub, int PRE = -1, bool FOLD = false,
-          bool CANON = false>
+          bool CANON = false, bool ROWT = false>
 __device__ __forceinline__ void run_passes(typename A::T* lds, int tid, const GetSub& get_sub) {
   constexpr Sched S = make_sched(LOGM);
+  static_assert(!ROWT || (LOGM == (int)kPermRowLog && S.np == 2 && S.s[1] == (int)kPermRowS0),
+                "the row-pass layout assumes rows of 2^8 in two radix-16 passes");
   if constexpr (P < S.np) {
     constexpr int idx = FWD ? P : S.np - 1 - P;
-    run_pass<A, FWD, LOGM, S.r[idx], S.s[idx], NSUB, NT, PRE, GetSub, FOLD && P == S.np - 1, CANON && P == 0>(
-        lds, tid, get_sub);
+    run_pass<A, FWD, LOGM, S.r[idx], S.s[idx], NSUB, NT, PRE, GetSub, FOLD && P == S.np - 1, CANON && P == 0,
+             ROWT && idx == S.np - 1>(lds, tid, get_sub);
     __syncthreads();
-    run_passes<A, FWD, LOGM, NSUB, NT, P + 1, GetSub, PRE, FOLD, CANON>(lds, tid, get_sub);
+    run_passes<A, FWD, LOGM, NSUB, NT, P + 1, GetSub, PRE, FOLD, CANON, ROWT>(lds, tid, get_sub);
   }
 }
 
@@ -589,8 +599,9 @@ __global__ __launch_bounds__(RowCfg<LOGN2>::NT) void ntt_row_kernel(uint64_t* __
     sp.prefix = (uint32_t)N1 + (GAL ? galois_row<LOGN1>((uint32_t)(r0 + sub), galois) : (uint32_t)(r0 + sub));
     return sp;
   };
+  constexpr bool kRowT = LOGN2 == (int)kPermRowLog && row_tw_permuted(LOGN1 + LOGN2);
   run_passes<A, FWD, LOGN2, kRows, NT, 0, decltype(get_sub), NNTT_ROW_FWD_PRELOAD ? 1 : -1, false,
-             !FWD && NNTT_CANON_FIRST>(lds, tid, get_sub);
+             !FWD && NNTT_CANON_FIRST, kRowT>(lds, tid, get_sub);
 
   static_assert((kRows * N2) % (2 * NT) == 0, "whole iterations");
 #pragma unroll
@@ -710,7 +721,8 @@ __global__ __launch_bounds__(RowCfg<LOGN2>::NT) void ntt_row_mac_kernel(uint64_t
     sp.prefix = (uint32_t)N1 + (uint32_t)(pl.tile * kRows + sub);
     return sp;
   };
-  run_passes<A, false, LOGN2, kRows, NT, 0, decltype(get_sub), -1, false, NNTT_CANON_FIRST>(lds, tid, get_sub);
+  run_passes<A, false, LOGN2, kRows, NT, 0, decltype(get_sub), -1, false, NNTT_CANON_FIRST,
+             LOGN2 == (int)kPermRowLog && row_tw_permuted(LOGN1 + LOGN2)>(lds, tid, get_sub);
 
   uint64_t* base = acc + row * N + off;
   static_assert((kRows * N2) % (2 * NT) == 0, "whole iterations");
@@ -806,7 +818,8 @@ __global__ __launch_bounds__(RowCfg<LOGN2>::NT) void ntt_row_mac_hoisted_kernel(
     sp.prefix = (uint32_t)N1 + (uint32_t)(pl.tile * kRows + sub);
     return sp;
   };
-  run_passes<A, false, LOGN2, kRows, NT, 0, decltype(get_sub), -1, false, NNTT_CANON_FIRST>(lds, tid, get_sub);
+  run_passes<A, false, LOGN2, kRows, NT, 0, decltype(get_sub), -1, false, NNTT_CANON_FIRST,
+             LOGN2 == (int)kPermRowLog && row_tw_permuted(LOGN1 + LOGN2)>(lds, tid, get_sub);
 
   uint64_t* base = acc + row * N + off;
 #pragma unroll

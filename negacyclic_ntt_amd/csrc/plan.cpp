@@ -12,6 +12,7 @@
 
 #include <algorithm>
 #include <new>
+#include <vector>
 
 #include "internal.h"
 
@@ -81,6 +82,24 @@ Barrett host_barrett(uint64_t q) {
   b.k = 64 - __builtin_clzll(q);
   b.mu = (uint64_t)(((u128)1 << (2 * b.k)) / q);
   return b;
+}
+
+// The row-pass layout of the two-pass split (internal.h, NNTT_ROW_TW_PERM) for one
+// prime's table t[0, 2^logn): within each stage block s >= log N1 + 4 and each row r,
+// entry (u, j) moves from u 2^v + j to j 2^4 + u (v = s - log N1 - 4).
+template <class Tw>
+static void permute_row_stages(Tw* t, uint32_t logn) {
+  const uint32_t logn1 = logn - kPermRowLog, n1 = 1u << logn1, g = 1u << kPermRowS0;
+  std::vector<Tw> tmp;
+  for (uint32_t s = logn1 + kPermRowS0; s < logn; ++s) {
+    const uint32_t v = s - logn1 - kPermRowS0, span = g << v;
+    for (uint32_t r = 0; r < n1; ++r) {
+      Tw* blk = t + (1u << s) + (size_t)r * span;
+      tmp.assign(blk, blk + span);
+      for (uint32_t u = 0; u < g; ++u)
+        for (uint32_t j = 0; j < (1u << v); ++j) blk[j * g + u] = tmp[(u << v) + j];
+    }
+  }
 }
 
 static unsigned bitrev(unsigned x, unsigned bits) {
@@ -274,6 +293,14 @@ extern "C" int ntt_plan_create(ntt_plan** out, uint32_t n, const uint64_t* prime
         fwd32[i] = Narrow::Tw{(uint32_t)w, (uint32_t)(((uint64_t)w << 32) / q)};
         inv32[i] = Narrow::Tw{(uint32_t)iw, (uint32_t)(((uint64_t)iw << 32) / q)};
       }
+    }
+    if (row_tw_permuted(p->logn)) {
+      permute_row_stages(fwd.data() + (size_t)l * n, p->logn);
+      permute_row_stages(inv.data() + (size_t)l * n, p->logn);
+      permute_row_stages(fwd60.data() + (size_t)l * n, p->logn);
+      permute_row_stages(inv60.data() + (size_t)l * n, p->logn);
+      permute_row_stages(fwd32.data() + (size_t)l * n, p->logn);
+      permute_row_stages(inv32.data() + (size_t)l * n, p->logn);
     }
     ModInfo& m = p->h_mods[l];
     memset(&m, 0, sizeof(m));
