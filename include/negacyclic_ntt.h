@@ -72,16 +72,25 @@ typedef struct ntt_plan ntt_plan;       /* opaque: n, primes, tables; immutable 
 typedef struct ntt_ks_plan ntt_ks_plan; /* opaque: key-switch constants; immutable */
 typedef struct ntt_mr_plan ntt_mr_plan; /* opaque: modraise constants; immutable */
 
-/* Human-readable name of a status code (static string). */
+/* Human-readable name of a status code (static string).  Errors are reported
+ * before launch, as FHElium validates before dispatch ("Eager, Compile, and
+ * native execution", section "Schema registration and device dispatch"). */
 const char *ntt_status_string(int status);
 
 /* Host utility: the first `count` primes q below 2^bits with q == 1 (mod 2n), in
  * descending order, written to out[0..count).  bits in [3, 62], n a power of two
- * in [2, 2^16].  NTT_EINVAL if fewer than `count` exist. */
+ * in [2, 2^16].  NTT_EINVAL if fewer than `count` exist.  The moduli are a
+ * caller-side parameter (FHElium "Eager, Compile, and native execution", section
+ * "Execution properties": modulus parameters enter native execution as arguments);
+ * this helper only picks the NTT-friendly ones the workloads use. */
 int ntt_find_primes(uint32_t bits, uint32_t n, uint32_t count, uint64_t *out);
 
 /* Create a plan for ring degree n (a power of two, 2 <= n <= 65536) and the
- * moduli primes[0..num_primes) (host array, copied).  Each prime must satisfy
+ * moduli primes[0..num_primes) (host array, copied).  The plan holds what FHElium
+ * passes to its native NTT as tensors -- modulus parameters and twiddle tables
+ * ("Eager, Compile, and native execution", section "Execution properties";
+ * section "Shared implementation and native path": parameter column j describes
+ * limb j) -- built once and kept on the device.  Each prime must satisfy
  * 3 <= q < 2^62, q == 1 (mod 2n), be prime (deterministic Miller-Rabin) and be
  * distinct from the others.  psi: optional host array of one primitive 2n-th
  * root per prime (psi^n == -1 mod q); NULL selects, per prime, the smallest
@@ -96,15 +105,23 @@ int ntt_plan_create(ntt_plan **out, uint32_t n, const uint64_t *primes, uint32_t
 
 /* Host copies of one prime's tables (each array n entries; any pointer may be
  * NULL to skip it): fwd[k] = psi^brv(k), fwd_shoup[k] = floor(fwd[k]*2^64/q),
- * inv[k] = psi^-brv(k), inv_shoup likewise.  *psi_out (nullable) gets psi. */
+ * inv[k] = psi^-brv(k), inv_shoup likewise.  *psi_out (nullable) gets psi.  These
+ * are the NTT and inverse tables of FHElium's native calls ("Eager, Compile, and
+ * native execution", section "Shared implementation and native path"), exposed
+ * so that callers and tests can check them.  NTT_EINVAL for limb >= num_primes. */
 int ntt_plan_get_tables(const ntt_plan *plan, uint32_t limb, uint64_t *psi_out, uint64_t *fwd, uint64_t *fwd_shoup,
                         uint64_t *inv, uint64_t *inv_shoup);
 
-/* n, number of primes and prime `limb` of a plan (for bindings). */
+/* n, number of primes and prime `limb` of a plan (for bindings): the parameter
+ * columns of FHElium's limb layout ("Eager, Compile, and native execution",
+ * section "Shared implementation and native path").  NTT_EINVAL on a NULL plan or
+ * an out-of-range limb. */
 int ntt_plan_info(const ntt_plan *plan, uint32_t *n, uint32_t *num_primes, int *device);
 int ntt_plan_prime(const ntt_plan *plan, uint32_t limb, uint64_t *q);
 
-/* Release a plan.  The caller guarantees no enqueued work still uses it. */
+/* Release a plan.  The caller guarantees no enqueued work still uses it: a
+ * stable address is not a completed use (FHElium, "Value signatures and reusable
+ * buffers", section "The writer cannot infer arbitrary readers"). */
 void ntt_plan_destroy(ntt_plan *plan);
 
 /* Forward negacyclic NTT, in place, on data[batch][num_limbs][n] (coefficient
@@ -116,7 +133,10 @@ int ntt_forward(const ntt_plan *plan, uint64_t *data, uint64_t batch, uint32_t l
                 void *stream);
 
 /* Inverse of ntt_forward, in place, including the n^-1 scaling (so that
- * ntt_inverse(ntt_forward(a)) == a). */
+ * ntt_inverse(ntt_forward(a)) == a): the inverse transform whose tables FHElium
+ * passes to its native NTT ("Eager, Compile, and native execution", section
+ * "Shared implementation and native path": NTT tables and inverse tables).  Same
+ * layout, alignment and errors as ntt_forward. */
 int ntt_inverse(const ntt_plan *plan, uint64_t *data, uint64_t batch, uint32_t limb_begin, uint32_t num_limbs,
                 void *stream);
 
@@ -196,7 +216,10 @@ void ntt_set_debug_checks(int on);
  * launch alone exceeds the cap is NTT_EUNSUPPORTED. */
 int ntt_set_max_launch_threads(uint64_t threads);
 
-/* Key-switch plan over a Q u P basis: the first num_q primes of qp_plan form Q
+/* Key-switch plan over a Q u P basis (the basis-extension and ModDown constants
+ * of FHElium's key-switch, "Eager, Compile, and native execution", section "CUDA
+ * execution"; they enter native execution as arguments, section "Execution
+ * properties"): the first num_q primes of qp_plan form Q
  * and the next num_p form P (num_q + num_p <= primes in qp_plan); Q is split into
  * dnum digits of num_q / dnum consecutive primes (num_q % dnum == 0,
  * num_q / dnum <= 16, num_p <= 16).  Precomputes the Garner (mixed-radix)
@@ -206,7 +229,10 @@ int ntt_set_max_launch_threads(uint64_t threads);
 int keyswitch_plan_create(ntt_ks_plan **out, const ntt_plan *qp_plan, uint32_t num_q, uint32_t num_p,
                           uint32_t dnum);
 
-/* Bytes of device workspace keyswitch needs for `batch` ciphertexts. */
+/* Bytes of device workspace keyswitch (and relinearize) need for `batch`
+ * ciphertexts.  The caller allocates it: FHElium leaves allocation to the caller's
+ * allocator ("Eager, Compile, and native execution", section "Execution
+ * properties").  NTT_EUNSUPPORTED for batch > 4096. */
 int keyswitch_workspace_size(const ntt_ks_plan *plan, uint64_t batch, size_t *bytes);
 
 /* Rotation key-switch (hybrid, dnum digits):
@@ -229,7 +255,9 @@ int keyswitch(const ntt_ks_plan *plan, uint64_t *out, const uint64_t *ct, const 
               uint64_t galois_elt, uint64_t batch, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Bytes of device workspace keyswitch_hoisted needs for num_rot rotations of `batch`
- * ciphertexts: batch * (dnum + 2 num_rot) * (num_q + num_p) * n * 8. */
+ * ciphertexts: batch * (dnum + 2 num_rot) * (num_q + num_p) * n * 8 (caller-owned,
+ * as for keyswitch_workspace_size).  NTT_EINVAL for num_rot 0, NTT_EUNSUPPORTED for
+ * num_rot > 64 or batch > 4096. */
 int keyswitch_hoisted_workspace_size(const ntt_ks_plan *plan, uint32_t num_rot, uint64_t batch, size_t *bytes);
 
 /* Hoisted rotations: num_rot Galois elements applied to the same ciphertexts with
@@ -268,6 +296,8 @@ int keyswitch_hoisted(const ntt_ks_plan *plan, uint64_t *out, const uint64_t *ct
 int relinearize(const ntt_ks_plan *plan, uint64_t *out, const uint64_t *d, const uint64_t *rlk, uint64_t batch,
                 void *workspace, size_t workspace_bytes, void *stream);
 
+/* Release a key-switch plan (caller guarantees no enqueued use, as for
+ * ntt_plan_destroy). */
 void keyswitch_plan_destroy(ntt_ks_plan *plan);
 
 /* ---- ModRaise ------------------------------------------------------------ */
@@ -278,8 +308,10 @@ void keyswitch_plan_destroy(ntt_ks_plan *plan);
  * must be a device plan and must outlive this plan. */
 int modraise_plan_create(ntt_mr_plan **out, const ntt_plan *plan, uint32_t num_from, uint32_t num_to);
 
-/* ModRaise, the first stage of the kestrel-llm bootstrapping profile (section 4.2:
- * a Garner extension raises the modulus chain back to the full chain).
+/* ModRaise: kestrel-llm data-flow overview, section 4.2 (the modraise stage that
+ * opens the bootstrapping profile).  Each coefficient's residues on the first
+ * num_from primes are lifted to their exact integer and re-reduced onto the longer
+ * chain.
  *   in  : [batch][num_from][n], coefficient domain;
  *   out : [batch][num_to][n]: out[t] = X mod q_t with X in [0, q_0 ... q_{from-1})
  *         the exact CRT value of the column (Garner's unsigned representative); the
@@ -287,6 +319,8 @@ int modraise_plan_create(ntt_mr_plan **out, const ntt_plan *plan, uint32_t num_f
  * out must not overlap in (NTT_EOVERLAP). */
 int modraise(const ntt_mr_plan *plan, uint64_t *out, const uint64_t *in, uint64_t batch, void *stream);
 
+/* Release a ModRaise plan (caller guarantees no enqueued use, as for
+ * ntt_plan_destroy). */
 void modraise_plan_destroy(ntt_mr_plan *plan);
 
 #ifdef __cplusplus

@@ -146,6 +146,22 @@ def _stream_ptr(t, stream):
     return _VP(torch.cuda.current_stream(t.device).cuda_stream)
 
 
+def _on_stream(t, stream):
+    """Context that makes `stream` torch's current stream on t's device (a no-op when
+    stream is None).  Temporaries a call allocates for itself (key-switch workspaces,
+    the count of non-canonical residues) are created inside it, so that torch's
+    caching allocator orders their reuse, and their initialisation and read-back, on
+    the stream the library launches on."""
+    import contextlib
+
+    import torch
+    if stream is None:
+        return contextlib.nullcontext()
+    if isinstance(stream, int):
+        stream = torch.cuda.ExternalStream(stream, device=t.device)
+    return torch.cuda.stream(stream)
+
+
 def _check_tensor(t, plan: Plan, name: str, lead: int = 0):
     """Validate a residue tensor and return (batch, num_limbs)."""
     import torch
@@ -230,10 +246,11 @@ def count_noncanonical(plan: Plan, x, limb_begin: int = 0, stream=None) -> int:
     """Number of residues of x [..., limbs, n] that are >= their prime (synchronises)."""
     import torch
     batch, limbs = _check_tensor(x, plan, "x")
-    cnt = torch.zeros(1, dtype=torch.int64, device=x.device)
-    _check(lib().ntt_count_noncanonical(plan.handle, _VP(x.data_ptr()), batch, limb_begin, limbs,
-                                        _VP(cnt.data_ptr()), _stream_ptr(x, stream)), "ntt_count_noncanonical")
-    return int(cnt.item())
+    with _on_stream(x, stream):  # zero fill, count and read-back all on the launch stream
+        cnt = torch.zeros(1, dtype=torch.int64, device=x.device)
+        _check(lib().ntt_count_noncanonical(plan.handle, _VP(x.data_ptr()), batch, limb_begin, limbs,
+                                            _VP(cnt.data_ptr()), _stream_ptr(x, stream)), "ntt_count_noncanonical")
+        return int(cnt.item())
 
 
 def set_debug_checks(on: bool):
@@ -311,7 +328,8 @@ def keyswitch(ks: KeySwitchPlan, out, ct, ksk, galois_elt: int, ws=None, stream=
     if tuple(ksk.shape) != (ks.dnum, 2, ks.num_q + ks.num_p, plan.n):
         raise ValueError("ksk must be [dnum, 2, num_q + num_p, n]")
     if ws is None:
-        ws = workspace(ks, batch)
+        with _on_stream(ct, stream):
+            ws = workspace(ks, batch)
     _check(lib().keyswitch(ks.handle, _VP(out.data_ptr()), _VP(ct.data_ptr()), _VP(ksk.data_ptr()), galois_elt,
                            batch, _VP(ws.data_ptr()), ws.numel() * ws.element_size(), _stream_ptr(ct, stream)),
            "keyswitch")
@@ -341,7 +359,8 @@ def keyswitch_hoisted(ks: KeySwitchPlan, out, ct, ksk, galois_elts, ws=None, str
     if tuple(ksk.shape) != (R, ks.dnum, 2, ks.num_q + ks.num_p, plan.n):
         raise ValueError("ksk must be [R, dnum, 2, num_q + num_p, n]")
     if ws is None:
-        ws = hoisted_workspace(ks, R, batch)
+        with _on_stream(ct, stream):
+            ws = hoisted_workspace(ks, R, batch)
     _gs_arr, gs_ptr = _u64arr(galois_elts)
     _check(lib().keyswitch_hoisted(ks.handle, _VP(out.data_ptr()), _VP(ct.data_ptr()), _VP(ksk.data_ptr()),
                                    gs_ptr, R, batch, _VP(ws.data_ptr()),
@@ -362,7 +381,8 @@ def relinearize(ks: KeySwitchPlan, out, d, rlk, ws=None, stream=None):
     if tuple(rlk.shape) != (ks.dnum, 2, ks.num_q + ks.num_p, plan.n):
         raise ValueError("rlk must be [dnum, 2, num_q + num_p, n]")
     if ws is None:
-        ws = workspace(ks, batch)
+        with _on_stream(d, stream):
+            ws = workspace(ks, batch)
     _check(lib().relinearize(ks.handle, _VP(out.data_ptr()), _VP(d.data_ptr()), _VP(rlk.data_ptr()), batch,
                              _VP(ws.data_ptr()), ws.numel() * ws.element_size(), _stream_ptr(d, stream)),
            "relinearize")

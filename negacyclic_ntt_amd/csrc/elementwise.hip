@@ -17,9 +17,6 @@ namespace nntt {
 namespace {
 
 constexpr int kThreads = 256;
-#ifndef NNTT_TENSOR_SUM_REDC
-#define NNTT_TENSOR_SUM_REDC 1
-#endif
 
 // Streaming 16-byte accesses: every residue is touched once, so loads and stores are
 // marked non-temporal (they bypass reuse-oriented cache allocation).
@@ -74,7 +71,6 @@ __global__ __launch_bounds__(kThreads) void tensor_kernel(uint64_t* __restrict__
   u64x2 r0, r1, r2;
   r0.x = barrett_mul(x0.x, y0.x, br);
   r0.y = barrett_mul(x0.y, y0.y, br);
-#if NNTT_TENSOR_SUM_REDC
   // d1 = a0 b1 + a1 b0: the exact 128-bit sum (< 2 q^2 < q 2^64) reduced once by
   // Montgomery (which divides by 2^64), then one Shoup product by 2^64 mod q.
   {
@@ -87,10 +83,6 @@ __global__ __launch_bounds__(kThreads) void tensor_kernel(uint64_t* __restrict__
     r1.x = csub(Wide::mul(redc(s0, q, mi.mont_ninv), r64, q), q);
     r1.y = csub(Wide::mul(redc(s1, q, mi.mont_ninv), r64, q), q);
   }
-#else
-  r1.x = add_mod(barrett_mul(x0.x, y1.x, br), barrett_mul(x1.x, y0.x, br), q);
-  r1.y = add_mod(barrett_mul(x0.y, y1.y, br), barrett_mul(x1.y, y0.y, br), q);
-#endif
   r2.x = barrett_mul(x1.x, y1.x, br);
   r2.y = barrett_mul(x1.y, y1.y, br);
   st_stream(d0, r0);
@@ -161,10 +153,8 @@ __global__ __launch_bounds__(kThreads) void automorph_coeff_multi_kernel(uint64_
 // of the per-element form, at the price of stores that fill half a line each (the
 // other half is the partner of another thread of the same limb, on the same XCD).
 // P pairs per thread; a block covers P * kThreads consecutive even outputs of one
-// row, so launched only when n / 2 is a multiple of that.
-#ifndef NNTT_AUTOMORPH_PAIR_NT
-#define NNTT_AUTOMORPH_PAIR_NT 0  // plain stores let the two halves of a line meet in L2 (non-temporal: +35%)
-#endif
+// row, so launched only when n / 2 is a multiple of that.  The stores are plain, so
+// that the two halves of a line meet in L2 (non-temporal stores: +35% on MI355X).
 template <uint32_t P>
 __global__ __launch_bounds__(kThreads) void automorph_coeff_pair_kernel(uint64_t* __restrict__ out,
                                                                         const uint64_t* __restrict__ in,
@@ -192,13 +182,8 @@ __global__ __launch_bounds__(kThreads) void automorph_coeff_pair_kernel(uint64_t
     const bool neg0 = i[k] >= n;
     const uint32_t o = (e[k] + g) & mask2n;
     const bool neg1 = neg0 != (o >= n);
-#if NNTT_AUTOMORPH_PAIR_NT
-    __builtin_nontemporal_store(neg0 ? neg_mod(v[k].x, q) : v[k].x, dst + e[k]);
-    __builtin_nontemporal_store(neg1 ? neg_mod(v[k].y, q) : v[k].y, dst + (o & (n - 1)));
-#else
     dst[e[k]] = neg0 ? neg_mod(v[k].x, q) : v[k].x;
     dst[o & (n - 1)] = neg1 ? neg_mod(v[k].y, q) : v[k].y;
-#endif
   }
 }
 
@@ -328,25 +313,23 @@ hipError_t launch_automorph(const ntt_plan* p, uint64_t* out, const uint64_t* in
                          in + b0 * poly, p->logn, (uint32_t)(g % two_n), nb * poly);
     });
   const uint32_t h = (uint32_t)host_invmod(g % two_n, two_n);
-#ifndef NNTT_AUTOMORPH_PER_THREAD
-#define NNTT_AUTOMORPH_PER_THREAD 2  // measured on MI355X: 2 beats 1 by 12% and 4 by 5%
-#endif
-  constexpr uint32_t kPer = NNTT_AUTOMORPH_PER_THREAD;
-#ifndef NNTT_AUTOMORPH_PAIRS
-#define NNTT_AUTOMORPH_PAIRS 1  // pairs per thread (0: off).  MI355X, 2^16 x 384 rows: 97 us; 2: 102, 4: 106; per-element form: 114
-#endif
-  constexpr uint32_t kPairs = NNTT_AUTOMORPH_PAIRS;
-  constexpr uint32_t kPairBlock = (kPairs ? kPairs : 1) * kThreads;  // even outputs per block
+  // Outputs per thread of the per-element forms (MI355X: 2 beats 1 by 12% and 4 by 5%)
+  // and pairs per thread of the pair form (2^16 x 384 rows: one pair 97 us, two 102,
+  // four 106; per-element form 114).  Rings whose half is a multiple of a pair block
+  // (n >= 512) take the pair form.
+  constexpr uint32_t kPer = 2;
+  constexpr uint32_t kPairs = 1;
+  constexpr uint32_t kPairBlock = kPairs * kThreads;  // even outputs per block
   const uint32_t half = p->n / 2, bpr = half / kPairBlock;
-  if (kPairs > 0 && bpr > 0 && half % kPairBlock == 0)
+  if (bpr > 0 && half % kPairBlock == 0)
     return in_parts(batch, (uint64_t)num_limbs * bpr * kThreads, [&](uint64_t b0, uint64_t nb) {
-      hipLaunchKernelGGL(automorph_coeff_pair_kernel<kPairs ? kPairs : 1>, dim3((uint32_t)(nb * num_limbs * bpr)),
+      hipLaunchKernelGGL(automorph_coeff_pair_kernel<kPairs>, dim3((uint32_t)(nb * num_limbs * bpr)),
                          dim3(kThreads), 0, s, out + b0 * poly, in + b0 * poly, p->d_mods, p->logn,
                          (uint32_t)(g % two_n), h, num_limbs, limb_begin, bpr);
     });
   return in_parts(batch, poly, [&](uint64_t b0, uint64_t nb) {
     const uint64_t total = nb * poly;
-    if (kPer > 1 && total % (kPer * kThreads) == 0)
+    if (total % (kPer * kThreads) == 0)
       hipLaunchKernelGGL(automorph_coeff_multi_kernel<kPer>, dim3(blocks_for(total / kPer)), dim3(kThreads), 0, s,
                          out + b0 * poly, in + b0 * poly, p->d_mods, p->logn, h, num_limbs, limb_begin, total / kPer);
     else
@@ -375,12 +358,9 @@ hipError_t launch_rescale(const ntt_plan* p, uint64_t* out, const uint64_t* in, 
   const uint32_t tiles = (p->n / 2 + kThreads - 1) / kThreads;
   // Enough blocks to fill the chip: split the output limbs into groups when the
   // batch is small (each group re-reads the dropped limb, one row of n words).
-#ifndef NNTT_RESCALE_BLOCKS
-#define NNTT_RESCALE_BLOCKS 2048
-#endif
+  constexpr uint64_t kRescaleBlocks = 2048;
   const uint64_t base = (uint64_t)tiles * batch;
-  const uint32_t want =
-      (uint32_t)std::min<uint64_t>(num_limbs - 1, (NNTT_RESCALE_BLOCKS + base - 1) / base);
+  const uint32_t want = (uint32_t)std::min<uint64_t>(num_limbs - 1, (kRescaleBlocks + base - 1) / base);
   const uint32_t groups = std::max(1u, want);
   for (uint64_t b0 = 0; b0 < batch; b0 += 65535) {
     const uint64_t nb = std::min<uint64_t>(65535, batch - b0);

@@ -44,11 +44,8 @@ constexpr uint32_t kMaxLogN = 16;
 // for each (v, j) the 16 sets of a row read 16 consecutive entries: each stage block
 // [2^s, 2^(s+1)) is permuted within each row's sub-block only.  Host copies returned
 // by ntt_plan_get_tables keep the plain order.
-#ifndef NNTT_ROW_TW_PERM
-#define NNTT_ROW_TW_PERM 1
-#endif
 constexpr uint32_t kPermMinLogN = 15, kPermRowLog = 8, kPermRowS0 = 4;
-__host__ __device__ constexpr bool row_tw_permuted(uint32_t logn) { return NNTT_ROW_TW_PERM && logn >= kPermMinLogN; }
+__host__ __device__ constexpr bool row_tw_permuted(uint32_t logn) { return logn >= kPermMinLogN; }
 
 // The NTT-domain automorphism in bit-reversed slot order: out[k] = in[slot(k)] with
 // 2 brv(slot) + 1 = (2 brv(k) + 1) g mod 2n, i.e. brv(slot) = g brv(k) + (g - 1) / 2

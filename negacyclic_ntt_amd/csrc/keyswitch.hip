@@ -40,21 +40,10 @@ constexpr int kKsThreads = 256;
 // extra waves: 28.8 us, two groups 29.6, four 40); ModDown in two groups of output
 // primes (one: 32, three: 30 us) whose loads are issued four limbs at a time (24.6 us;
 // eight: 25.7, twelve: 29.8).  Primes at or above 2^60 keep two ModUp groups.
-#ifndef NNTT_MODUP_GROUPS
-#define NNTT_MODUP_GROUPS 1
-#endif
-#ifndef NNTT_MODUP_GROUPS_WIDE
-#define NNTT_MODUP_GROUPS_WIDE 2
-#endif
-#ifndef NNTT_MODDOWN_CH
-#define NNTT_MODDOWN_CH 4
-#endif
-#ifndef NNTT_MODDOWN_GROUPS
-#define NNTT_MODDOWN_GROUPS 2
-#endif
-constexpr uint32_t kModUpGroups = NNTT_MODUP_GROUPS;
-constexpr uint32_t kModUpGroupsWide = NNTT_MODUP_GROUPS_WIDE;
-constexpr uint32_t kModDownGroups = NNTT_MODDOWN_GROUPS;
+constexpr uint32_t kModUpGroups = 1;
+constexpr uint32_t kModUpGroupsWide = 2;
+constexpr uint32_t kModDownGroups = 2;
+constexpr int kModDownChunk = 4;
 constexpr int kMaxDigitPrimes = 16;  // table row strides of the device constants
 constexpr int kMaxSpecial = 16;
 
@@ -360,10 +349,7 @@ __global__ __launch_bounds__(kKsThreads) void mac_hoisted_kernel(uint64_t* __res
   __syncthreads();
   if (!active) return;
   const uint64_t q = mods[t].q, ninv = mods[t].mont_ninv;
-#ifndef NNTT_HOIST_UNROLL
-#define NNTT_HOIST_UNROLL 2
-#endif
-#pragma unroll NNTT_HOIST_UNROLL
+#pragma unroll 2
   for (uint32_t r = 0; r < R; ++r) {
     const uint32_t g = ha.g[r];
     const uint32_t k0 = (ntt_slot(s0, ha.h[r], logn) & ~(seg - 1)) + i2;
@@ -435,7 +421,7 @@ __global__ __launch_bounds__(kKsThreads) void moddown_kernel(uint64_t* __restric
   const uint32_t l0 = grp * per, l1 = min(nq, l0 + per);
   // The output limbs go in chunks whose loads (accumulator residue, gathered addend)
   // are all issued together; the first chunk's before the Garner digits are computed.
-  constexpr int CH = NNTT_MODDOWN_CH;
+  constexpr int CH = kModDownChunk;
   uint64_t av[CH], cv[CH];
   auto prefetch = [&](uint32_t lb) {
 #pragma unroll
@@ -732,12 +718,9 @@ int ks_check(const ntt_ks_plan* p, uint64_t* out, const KsIo& io, const uint64_t
   return NTT_OK;
 }
 
-#ifndef NNTT_KS_EXACT
-#define NNTT_KS_EXACT 1
-#endif
 template <bool B60, int K>
 void launch_modup(dim3 grid, hipStream_t s, uint64_t* ext, const KsIo& io, const ntt_ks_plan* p, uint32_t h) {
-  if (NNTT_KS_EXACT && p->alpha == (uint32_t)K)
+  if (p->alpha == (uint32_t)K)
     hipLaunchKernelGGL((modup_kernel<B60, K, true>), grid, dim3(kKsThreads), 0, s, ext, io.src, io.src_stride,
                        p->dev, p->qp->logn, h, p->nq, p->np, p->alpha, p->dnum);
   else
@@ -748,7 +731,7 @@ void launch_modup(dim3 grid, hipStream_t s, uint64_t* ext, const KsIo& io, const
 template <bool B60, int KP>
 void launch_moddown(dim3 grid, hipStream_t s, uint64_t* out, const uint64_t* acc, const KsIo& io,
                     const ntt_ks_plan* p, uint32_t groups, uint64_t out_rot, uint64_t acc_rot, const HoistArgs& ha) {
-  if (NNTT_KS_EXACT && p->np == (uint32_t)KP)
+  if (p->np == (uint32_t)KP)
     hipLaunchKernelGGL((moddown_kernel<B60, KP, true>), grid, dim3(kKsThreads), 0, s, out, acc, io.add,
                        io.add_stride, io.add_mask, p->dev, p->qp->logn, p->nq, p->np, groups, out_rot, acc_rot, ha);
   else

@@ -36,18 +36,9 @@
 namespace nntt {
 namespace {
 
-// Register radix (log2) of one pass, and the column / row tile of the two-pass
-// split.  Compile-time tuning knobs; the defaults are the measured best on gfx950.
-#ifndef NNTT_MAX_RADIX_LOG
-#define NNTT_MAX_RADIX_LOG 4
-#endif
-#ifndef NNTT_COL_TILE
-#define NNTT_COL_TILE 16
-#endif
-#ifndef NNTT_ROW_TILE
-#define NNTT_ROW_TILE 16
-#endif
-constexpr int kMaxRadixLog = NNTT_MAX_RADIX_LOG;
+// Register radix (log2) of one pass: radix-16 sets (16 residues per thread).  On
+// MI355X radix 2^2..2^5 were measured; radix 32 no longer fits the register file.
+constexpr int kMaxRadixLog = 4;
 
 // Split m stages into passes of at most kMaxRadixLog, as even as possible.
 struct Sched {
@@ -67,35 +58,16 @@ constexpr Sched make_sched(int logm) {
   return S;
 }
 
-#ifndef NNTT_ROW_FWD_PRELOAD
-#define NNTT_ROW_FWD_PRELOAD 1  // MI355X: bench step +1.4%, forward -2%, key-switch -2.6%
-#endif
-#ifndef NNTT_COL_FWD_PRELOAD
-#define NNTT_COL_FWD_PRELOAD 1  // MI355X: forward -0.7% in the bench step, -1.6% back to back
-#endif
-#ifndef NNTT_COL_TW_LDS
-#define NNTT_COL_TW_LDS 0  // MI355X: staging in LDS ties in the bench step, 4-5% slower back to back
-#endif
-#ifndef NNTT_LDS_PAD
-#define NNTT_LDS_PAD 1
-#endif
-#ifndef NNTT_INV_FOLD
-#define NNTT_INV_FOLD 1  // the column pass of the inverse folds n^-1 into its last stage
-#endif
-#ifndef NNTT_CANON_FIRST
-#define NNTT_CANON_FIRST 1  // a transform's first stage takes canonical inputs unreduced
-#endif
-#ifndef NNTT_SPLIT_MIN_LOGN
-#define NNTT_SPLIT_MIN_LOGN 15  // smallest ring that uses the two-pass split
-#endif
+// LDS rows are padded by one slot per 2^kPadShift residues (and one more per row), so
+// that the strided set accesses of a pass spread over the banks.
 template <class A>
 constexpr int sub_stride(int m) {
-  return NNTT_LDS_PAD ? (1 << m) + ((1 << m) >> A::kPadShift) + 1 : (1 << m);
+  return (1 << m) + ((1 << m) >> A::kPadShift) + 1;
 }
 
 template <class A>
 __device__ __forceinline__ int lpos(int pos) {
-  return NNTT_LDS_PAD ? pos + (pos >> A::kPadShift) : pos;
+  return pos + (pos >> A::kPadShift);
 }
 
 // Work placement.  The logical block lb = xcd_local_block(b) (internal.h) gives each
@@ -401,7 +373,7 @@ __global__ __launch_bounds__(LdsCfg<LOGN>::NT) void ntt_lds_kernel(uint64_t* dat
   // Inverse: twiddles on demand (measured on MI355X: n = 2^14, 2048 limbs, 307 -> 291 us;
   // the same at n = 2048).  The n^-1 scaling stays in the store: folded into the last
   // stage as in the column pass it was 1% slower at n = 2^14.
-  run_passes<A, FWD, LOGN, ROWS, NT, 0, decltype(get_sub), 0, false, NNTT_CANON_FIRST>(lds, tid, get_sub);
+  run_passes<A, FWD, LOGN, ROWS, NT, 0, decltype(get_sub), 0, false, true>(lds, tid, get_sub);
 
   static_assert((ROWS * N) % (2 * NT) == 0, "whole iterations");
 #pragma unroll
@@ -434,8 +406,8 @@ __device__ __forceinline__ ulonglong2 load_tile(const uint64_t* p) {
 // Two-pass split for n = N1 * N2 (N2 contiguous).  Column kernel: a workgroup
 // owns COLS adjacent columns (COLS * 8 B = one 128 B line per row) of one limb.
 // Row kernel: a workgroup owns ROWS consecutive rows of one limb.
-constexpr int kCols = NNTT_COL_TILE;
-constexpr int kRows = NNTT_ROW_TILE;
+constexpr int kCols = 16;
+constexpr int kRows = 16;
 
 template <int LOGN1>
 struct ColCfg {
@@ -515,26 +487,14 @@ __global__ __launch_bounds__(ColCfg<LOGN1>::NT) void ntt_col_kernel(uint64_t* da
 
   const ModInfo& m = mods[limb];
   SubParams<A> sp;
-#if NNTT_COL_TW_LDS
-  // A column transform (prefix 1) uses table entries below N1 only: stage them in LDS.
-  __shared__ typename A::Tw tw_lds[N1];
-  {
-    const typename A::Tw* tg = table_of<A>(tw_all, limb, N);
-    for (int i = tid; i < N1; i += NT) tw_lds[i] = tg[i];
-  }
-  __syncthreads();
-  sp.tw = tw_lds;
-#else
   sp.tw = table_of<A>(tw_all, limb, N);
-#endif
   sp.q = modulus<A>(m);
   sp.prefix = 1;
   // The inverse's last launch folds n^-1 into its last stage.
-  constexpr bool kFold = !FWD && LAST && NNTT_INV_FOLD;
+  constexpr bool kFold = !FWD && LAST;
   if constexpr (kFold) scaled_last_stage<A>(m, sp.ninv, sp.w1n);
   auto get_sub = [&](int) { return sp; };
-  run_passes<A, FWD, LOGN1, kCols, NT, 0, decltype(get_sub), NNTT_COL_FWD_PRELOAD ? 1 : -1, kFold,
-             FWD && NNTT_CANON_FIRST>(lds, tid, get_sub);
+  run_passes<A, FWD, LOGN1, kCols, NT, 0, decltype(get_sub), 1, kFold, FWD>(lds, tid, get_sub);
 
   static_assert((kCols * N1) % (2 * NT) == 0, "whole iterations");
 #pragma unroll
@@ -600,8 +560,7 @@ __global__ __launch_bounds__(RowCfg<LOGN2>::NT) void ntt_row_kernel(uint64_t* __
     return sp;
   };
   constexpr bool kRowT = LOGN2 == (int)kPermRowLog && row_tw_permuted(LOGN1 + LOGN2);
-  run_passes<A, FWD, LOGN2, kRows, NT, 0, decltype(get_sub), NNTT_ROW_FWD_PRELOAD ? 1 : -1, false,
-             !FWD && NNTT_CANON_FIRST, kRowT>(lds, tid, get_sub);
+  run_passes<A, FWD, LOGN2, kRows, NT, 0, decltype(get_sub), 1, false, !FWD, kRowT>(lds, tid, get_sub);
 
   static_assert((kRows * N2) % (2 * NT) == 0, "whole iterations");
 #pragma unroll
@@ -640,10 +599,7 @@ struct MacSrc {
 
 // Key residues are read once per launch: non-temporal loads keep them from evicting
 // the digits, which the hoisted product reads once per rotation and component.
-#ifndef NNTT_MAC_KEY_NT
-#define NNTT_MAC_KEY_NT 1
-#endif
-__device__ __forceinline__ ulonglong2 load_key(const uint64_t* p) { return load_tile<NNTT_MAC_KEY_NT != 0>(p); }
+__device__ __forceinline__ ulonglong2 load_key(const uint64_t* p) { return load_tile<true>(p); }
 
 // DN > 0: dnum == DN and DN products fit one reduction (all loads of an element pair
 // are issued before any arithmetic); DN == 0: any dnum, chunked reductions.
@@ -721,7 +677,7 @@ __global__ __launch_bounds__(RowCfg<LOGN2>::NT) void ntt_row_mac_kernel(uint64_t
     sp.prefix = (uint32_t)N1 + (uint32_t)(pl.tile * kRows + sub);
     return sp;
   };
-  run_passes<A, false, LOGN2, kRows, NT, 0, decltype(get_sub), -1, false, NNTT_CANON_FIRST,
+  run_passes<A, false, LOGN2, kRows, NT, 0, decltype(get_sub), -1, false, true,
              LOGN2 == (int)kPermRowLog && row_tw_permuted(LOGN1 + LOGN2)>(lds, tid, get_sub);
 
   uint64_t* base = acc + row * N + off;
@@ -818,7 +774,7 @@ __global__ __launch_bounds__(RowCfg<LOGN2>::NT) void ntt_row_mac_hoisted_kernel(
     sp.prefix = (uint32_t)N1 + (uint32_t)(pl.tile * kRows + sub);
     return sp;
   };
-  run_passes<A, false, LOGN2, kRows, NT, 0, decltype(get_sub), -1, false, NNTT_CANON_FIRST,
+  run_passes<A, false, LOGN2, kRows, NT, 0, decltype(get_sub), -1, false, true,
              LOGN2 == (int)kPermRowLog && row_tw_permuted(LOGN1 + LOGN2)>(lds, tid, get_sub);
 
   uint64_t* base = acc + row * N + off;
@@ -970,18 +926,8 @@ hipError_t launch_any(const ntt_plan* p, uint64_t* data, const uint64_t* in, uin
     NNTT_CASE(10)
     NNTT_CASE(11)
     NNTT_CASE(12)
-#if NNTT_SPLIT_MIN_LOGN > 13
     NNTT_CASE(13)
-#else
-    case 13:
-      return launch_split<A, 6, 7>(p, data, in, rows, limb_begin, num_limbs, op, g, s);
-#endif
-#if NNTT_SPLIT_MIN_LOGN > 14
     NNTT_CASE(14)
-#else
-    case 14:
-      return launch_split<A, 7, 7>(p, data, in, rows, limb_begin, num_limbs, op, g, s);
-#endif
 #undef NNTT_CASE
     case 15:
       return launch_split<A, 7, 8>(p, data, in, rows, limb_begin, num_limbs, op, g, s);

@@ -84,7 +84,7 @@ Barrett host_barrett(uint64_t q) {
   return b;
 }
 
-// The row-pass layout of the two-pass split (internal.h, NNTT_ROW_TW_PERM) for one
+// The row-pass layout of the two-pass split (internal.h, row_tw_permuted) for one
 // prime's table t[0, 2^logn): within each stage block s >= log N1 + 4 and each row r,
 // entry (u, j) moves from u 2^v + j to j 2^4 + u (v = s - log N1 - 4).
 template <class Tw>

@@ -161,8 +161,9 @@ int orc_relinearize(uint64_t *out, const uint64_t *d, const uint64_t *rlk, uint6
 int orc_rescale(uint64_t *out, const uint64_t *in, int mode, uint64_t batch, uint32_t limbs, uint64_t n,
                 const uint64_t *primes);
 
-/* ModRaise (the first stage of the kestrel-llm bootstrapping profile, section 4.2:
- * a Garner extension raises the modulus chain back to the full chain).
+/* ModRaise: kestrel-llm data-flow overview, section 4.2 (the modraise stage that
+ * opens the bootstrapping profile).  Each coefficient is lifted to its exact
+ * integer on the first `from` primes and re-reduced onto the longer chain.
  * in: [batch][from][n] coefficient domain modulo primes[0..from); out:
  * [batch][to][n] modulo primes[0..to), to > from: out[t] = X mod primes[t] with X the
  * exact CRT value of the column in [0, prod_{i<from} primes[i]) (the unsigned

@@ -222,3 +222,43 @@ def test_graph_capture_replays_match_eager(B):
         assert_bits_equal(host(c), want_c, f"replay {rep} pipeline")
         assert_bits_equal(host(ko), want_k, f"replay {rep} keyswitch")
         B.ntt_forward(plan, dev(residues((2, 24, n), qp[:24], 9960 + rep)))  # eager work between replays
+
+
+@pytest.mark.parametrize("as_int", [False, True])
+def test_explicit_side_stream_without_workspace(B, as_int):
+    """stream= names a stream other than torch's current one and no workspace is
+    passed: the workspace the binding allocates, and the counter of
+    count_noncanonical, are ordered on that stream.  Between calls the current stream
+    allocates and fills tensors of the workspace's size, which would take over a
+    workspace released to the current stream while the side stream still used it."""
+    import torch
+    n, nq, npr, dnum, g = 1 << 12, 6, 2, 3, 5
+    qp, plan, ks = _setup(B, n, nq, npr, dnum)
+    ct = residues((2, 2, nq, n), qp[:nq], 9401)
+    ksk = residues((dnum, 2, nq + npr, n), qp[: nq + npr], 9402)
+    want = orc.keyswitch(ct, ksk, g, qp[: nq + npr], nq, dnum)
+    dct, dksk = dev(ct), dev(ksk)
+    side = torch.cuda.Stream()
+    stream = side.cuda_stream if as_int else side
+    ws_elems = ks.workspace_bytes(2) // 8
+    outs = []
+    for rep in range(3):
+        out = torch.zeros_like(dct)
+        side.wait_stream(torch.cuda.current_stream())
+        announce("keyswitch on a side stream, binding workspace", rep, as_int)
+        B.keyswitch(ks, out, dct, dksk, g, stream=stream)
+        out.record_stream(side)
+        outs.append(out)
+        torch.empty(ws_elems, dtype=torch.int64, device="cuda:0").fill_(-1)  # current stream
+    side.synchronize()
+    torch.cuda.synchronize()
+    for rep, out in enumerate(outs):
+        assert_bits_equal(host(out), want, f"side-stream keyswitch {rep}")
+    bad = ct.copy()
+    bad[0, 1, 2, 7] = qp[2]          # exactly q: not canonical
+    bad[1, 0, 5, 100] = qp[5] + 3
+    dbad = dev(bad)
+    torch.cuda.synchronize()
+    announce("count_noncanonical on a side stream", as_int)
+    assert B.count_noncanonical(plan, dbad.view(-1, nq, n), stream=stream) == 2
+    assert B.count_noncanonical(plan, dct.view(-1, nq, n), stream=stream) == 0
