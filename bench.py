@@ -8,13 +8,19 @@ polynomials, tensor [8][2][24][65536], seeded uniform residues):
   2. pointwise product  C = A_hat * B_hat              (NTT domain)
   3. ciphertext tensor product D = (A_hat, B_hat)      ([8][3][24][n])
   4. inverse NTT of C                                  (384 limb-INTTs)
-  5. coefficient-domain automorphism E = sigma_g(C), g = 5^(2^(s mod 16)) mod 2n
+  5. coefficient-domain automorphism E = sigma_g(B'), g = 5^(2^(s mod 16)) mod 2n, of
+     the B operand of another input set (not written or read for a whole step)
   6. one rotation key-switch of a 1-ciphertext batch (Q = 24, P = 8, dnum = 3)
-     with the same g (96 forward + 64 inverse limb transforms inside)
+     with the same g (96 forward + 64 inverse limb transforms inside), over ten
+     distinct ciphertexts and keys in turn
 `value` is limb-NTTs per second over whole steps (forward and inverse
 transforms, those inside the key-switch included).  Inputs are resident in HBM
 before timing; the timed steps rotate over enough distinct buffers and keys
-(> 1 GB) that the 256 MB Infinity Cache cannot hold them.
+(> 2 GB) that the 256 MB Infinity Cache cannot hold them.
+
+`roofline` is the forward NTT's algorithmic HBM rate against the 8 TB/s peak;
+`alu_issue` gives the same call against the 32-bit multiply issue peak, with the
+clock that peak assumes and the clock sampled during the timed steps.
 """
 import argparse
 import json
@@ -60,21 +66,41 @@ def kernel_sources_digest(read=None):
     return h.hexdigest()[:16]
 
 
-def recorded_traffic():
-    """HBM bytes per forward-NTT call from the committed counter summary, if it was
-    taken on the current kernel sources (else None)."""
-    path = os.path.join(PROFILES, "ntt_forward_n65536_q24x60_traffic.md")
+def recorded_fields(name):
+    """The `- key: value` fields of a committed counter summary under profiles/, if it
+    was taken on the current kernel sources (its kernel_sources_sha256_16 matches the
+    code text of modarith.h + ntt.hip); else {}."""
+    path = os.path.join(PROFILES, name)
     if not os.path.exists(path):
-        return None
+        return {}
     fields = {}
     for line in open(path):
         if line.startswith("- ") and ":" in line:
             k, v = line[2:].split(":", 1)
             fields[k.strip()] = v.strip().strip("`")
     if fields.get("kernel_sources_sha256_16") != kernel_sources_digest():
-        return None
+        return {}
+    return fields
+
+
+def recorded_traffic():
+    """HBM bytes per forward-NTT call from the committed counter summary, if it was
+    taken on the current kernel sources (else None)."""
     try:
-        return int(fields["hbm_bytes_per_call"])
+        return int(recorded_fields("ntt_forward_n65536_q24x60_traffic.md")["hbm_bytes_per_call"])
+    except (KeyError, ValueError):
+        return None
+
+
+def recorded_valu():
+    """VALU instructions per butterfly and VALUBusy of the forward NTT's two passes from
+    the committed counter summary (current kernel sources only; else None)."""
+    f = recorded_fields("ntt_forward_n65536_q24x60_valu.md")
+    try:
+        return {"valu_insts_per_butterfly_col": float(f["valu_insts_per_butterfly_col"]),
+                "valu_insts_per_butterfly_row": float(f["valu_insts_per_butterfly_row"]),
+                "valu_busy_pct_col": float(f["valu_busy_pct_col"]),
+                "valu_busy_pct_row": float(f["valu_busy_pct_row"])}
     except (KeyError, ValueError):
         return None
 
@@ -85,6 +111,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--rotate", type=int, default=3, help="distinct input sets cycled through")
+    ap.add_argument("--ks-rotate", type=int, default=10,
+                    help="distinct key-switch ciphertexts and keys cycled through (100.7 MB per key)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-next-rows", action="store_true", help="skip relin / rescale / hoisted / modraise timings")
     ap.add_argument("--no-other-configs", action="store_true", help="skip the n = 2^14 and n = 2048 workloads")
@@ -97,22 +125,21 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(primes, n, nq, npr, dnum, sample_limbs, a_host, b_host, ct_host, ksk_host, g, min_seconds=10.0,
-                 max_passes=40):
-    """The plain-C oracle on a bounded sample of one step, timed on the host cores."""
+def oracle_step_sample(primes, n, nq, npr, dnum, rows, a_host, b_host, ct_host, ksk_host, g, threads, min_seconds,
+                       max_passes):
+    """Whole passes of the step's operations on `rows` polynomials plus one key-switch,
+    repeated until at least min_seconds of CPU work.  Returns (limb transforms, seconds,
+    passes)."""
     import numpy as np
 
     import oracle as orc
-    threads = orc.default_threads()
     L = nq
-    rows = max(2, min(a_host.size // (L * n), sample_limbs // L))  # whole polynomials of the batch
     a = np.ascontiguousarray(a_host.reshape(-1, L, n)[:rows])
     b = np.ascontiguousarray(b_host.reshape(-1, L, n)[:rows])
     qs = primes[:L]
     per_pass = 2 * rows * L + dnum * (nq + npr) + 2 * (nq + npr)
     passes = 0
     t0 = time.perf_counter()
-    # Whole passes until at least min_seconds of CPU work (bounded by max_passes).
     while passes < max_passes and (passes == 0 or time.perf_counter() - t0 < min_seconds):
         ah = orc.batch_ntt(a, qs, threads=threads)
         c = orc.batch_pointwise(ah, b, qs)
@@ -122,15 +149,36 @@ def cpu_baseline(primes, n, nq, npr, dnum, sample_limbs, a_host, b_host, ct_host
         orc.batch_automorph(c, g, 0, qs)
         orc.keyswitch(ct_host, ksk_host, g, primes[: nq + npr], nq, dnum, threads=threads)
         passes += 1
-    dt = time.perf_counter() - t0
-    limb_ntts = per_pass * passes
+    return per_pass * passes, time.perf_counter() - t0, passes
+
+
+def cpu_baseline(primes, n, nq, npr, dnum, sample_limbs, a_host, b_host, ct_host, ksk_host, g, min_seconds=10.0,
+                 max_passes=40):
+    """The plain-C oracle on a bounded sample of one step, timed on the host cores: all
+    of them (the reported value), and one core on a smaller sample."""
+    import oracle as orc
+    threads = orc.default_threads()
+    L = nq
+    rows = max(2, min(a_host.size // (L * n), sample_limbs // L))  # whole polynomials of the batch
+    work, dt, passes = oracle_step_sample(primes, n, nq, npr, dnum, rows, a_host, b_host, ct_host, ksk_host, g,
+                                          threads, min_seconds, max_passes)
+    rows1 = 2
+    work1, dt1, passes1 = oracle_step_sample(primes, n, nq, npr, dnum, rows1, a_host, b_host, ct_host, ksk_host, g,
+                                             1, min_seconds / 2, max_passes)
     return {
-        "value": limb_ntts / dt,
+        "value": work / dt,
         "unit": "limb-NTT/s",
         "cores": threads,
         "kind": "oracle",
         "sample": (f"{passes} passes over {rows} of the 16 polynomials (forward NTT, pointwise, tensor, inverse "
-                   f"NTT, automorphism) plus one key-switch: {limb_ntts} limb transforms in {dt:.1f} s"),
+                   f"NTT, automorphism) plus one key-switch: {work} limb transforms in {dt:.1f} s"),
+        "single_core": {
+            "value": work1 / dt1,
+            "unit": "limb-NTT/s",
+            "cores": 1,
+            "sample": (f"{passes1} passes over {rows1} polynomials plus one key-switch, one thread: {work1} limb "
+                       f"transforms in {dt1:.1f} s"),
+        },
     }
 
 
@@ -247,6 +295,27 @@ def time_graph(fns, replays=5):
     return e0.elapsed_time(e1) / (replays * len(fns))
 
 
+def galois_rows(B, plan, sets, E, galois, reps):
+    """The forward NTT with sigma_g folded into its loads (ntt_forward_galois, in place)
+    for each of the 16 Galois elements of the large-ring workload, next to the plain
+    forward NTT timed the same way, and the coefficient-domain automorphism of each g.
+    Calls rotate over the input sets, so an input was last touched two calls (> 400 MB)
+    earlier."""
+    fwd = time_cycle([lambda a=a: B.ntt_forward(plan, a) for a, _ in sets], max(reps, 2 * len(sets)))
+    gal, aut = {}, {}
+    for g in galois:
+        gal[str(g)] = round(1e3 * time_cycle([lambda a=a, g=g: B.ntt_forward_galois(plan, a, a, g) for a, _ in sets],
+                                             max(reps, 2 * len(sets))), 2)
+        aut[str(g)] = round(1e3 * time_cycle([lambda b=b, g=g: B.automorph(plan, E, b, g, 0) for _, b in sets],
+                                             max(reps, 2 * len(sets))), 2)
+    gm, am = sum(gal.values()) / len(gal), sum(aut.values()) / len(aut)
+    elem = sets[0][0].numel()
+    return {"ntt_forward_us": round(fwd * 1e3, 2), "ntt_forward_galois_us": gal,
+            "ntt_forward_galois_mean_us": round(gm, 2), "galois_over_plain": round(gm / (fwd * 1e3), 4),
+            "automorph_coeff_us": aut, "automorph_coeff_mean_us": round(am, 2),
+            "automorph_coeff_alg_GBps": round(16 * elem / (am * 1e-6) / 1e9, 1)}
+
+
 def other_configs(B, reps):
     """Per-call times on the three smaller workloads (their parity is tested; these
     numbers are context, not part of `value`).  Operands rotate through copies of
@@ -321,10 +390,104 @@ def device_info():
     p = torch.cuda.get_device_properties(0)
     info = {"name": p.name, "arch": getattr(p, "gcnArchName", None), "cus": p.multi_processor_count,
             "hbm_GB": round(p.total_memory / 1e9, 1), "hip": torch.version.hip, "torch": torch.__version__}
-    clock = getattr(p, "clock_rate", None)
-    if clock:
-        info["clock_MHz"] = round(clock / 1e3)
+    peak = hip_clock_rate_khz()
+    if peak:
+        info["peak_sclk_MHz"] = round(peak / 1e3)
     return info
+
+
+def hip_clock_rate_khz():
+    """hipDeviceAttributeClockRate of device 0 (the peak shader clock, kHz), or None."""
+    import ctypes
+    import re
+    try:
+        hdr = open("/opt/rocm/include/hip/hip_runtime_api.h").read()
+        body = hdr[hdr.index("typedef enum hipDeviceAttribute_t"):]
+        body = body[body.index("{") + 1: body.index("}")]
+        idx, value, seen = None, -1, {}
+        for line in re.sub(r"//[^\n]*|/\*.*?\*/", "", body, flags=re.S).split(","):
+            m = re.match(r"\s*(\w+)\s*(?:=\s*(\w+))?\s*$", line)
+            if not m:
+                continue
+            if m.group(2):  # an explicit value: a number or an earlier enumerator
+                value = seen[m.group(2)] if m.group(2) in seen else int(m.group(2), 0)
+            else:
+                value += 1
+            seen[m.group(1)] = value
+            if m.group(1) == "hipDeviceAttributeClockRate":
+                idx = value
+                break
+        if idx is None:
+            return None
+        lib = ctypes.CDLL("libamdhip64.so")
+        v = ctypes.c_int(0)
+        if lib.hipDeviceGetAttribute(ctypes.byref(v), idx, 0) != 0 or v.value <= 0:
+            return None
+        return v.value
+    except (OSError, ValueError, AttributeError):
+        return None
+
+
+class ClockSampler:
+    """Samples the current shader clock (the starred level of the GPU's pp_dpm_sclk in
+    sysfs) every 2 ms in a background thread while the timed steps run."""
+
+    def __init__(self):
+        import glob
+        import threading
+        self.path = self._find(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.samples = []
+        self._stop = threading.Event()
+        self._t = threading.Thread(target=self._run, daemon=True) if self.path else None
+
+    @staticmethod
+    def _find(paths):
+        import torch
+        try:
+            props = torch.cuda.get_device_properties(0)
+            bus = getattr(props, "pci_bus_id", None)
+        except RuntimeError:
+            bus = None
+        for pth in sorted(paths):
+            dev = os.path.realpath(os.path.dirname(pth))
+            if bus is None and len(paths) == 1:
+                return pth
+            if bus is not None and os.path.basename(dev).split(":")[-2:-1] == [f"{bus:02x}"]:
+                return pth
+        return None
+
+    def _read(self):
+        try:
+            for line in open(self.path):
+                if line.rstrip().endswith("*"):
+                    return int("".join(ch for ch in line.split(":", 1)[1] if ch.isdigit()))
+        except (OSError, ValueError, IndexError):
+            return None
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = self._read()
+            if v:
+                self.samples.append(v)
+            self._stop.wait(0.002)
+
+    def __enter__(self):
+        if self._t:
+            self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._t:
+            self._stop.set()
+            self._t.join()
+
+    def summary(self):
+        if not self.samples:
+            return {"source": self.path, "samples": 0}
+        v = sorted(self.samples)
+        return {"source": self.path, "samples": len(v), "min_MHz": v[0], "median_MHz": v[len(v) // 2],
+                "max_MHz": v[-1]}
 
 
 def sustained(B, calls):
@@ -385,7 +548,9 @@ def main():
     sets = [(a0, b0)] + [(a0.clone(), b0.clone()) for _ in range(args.rotate - 1)]
     ct = B.to_device(ct_host)
     ksk0 = B.to_device(ksk_host)
-    keys = [ksk0] + [ksk0.clone() for _ in range(max(0, 2 * args.rotate - 1))]
+    nks = max(1, args.ks_rotate)
+    keys = [ksk0] + [ksk0.clone() for _ in range(nks - 1)]
+    cts = [ct] + [ct.clone() for _ in range(nks - 1)]
     C = torch.empty_like(a0)
     E = torch.empty_like(a0)
     D = torch.empty((W.shape_a[0], 3, L, n), dtype=torch.int64, device=dev)
@@ -403,7 +568,8 @@ def main():
     del cal_src, cal_dst
     torch.cuda.synchronize()
     gen_s = time.perf_counter() - t_gen
-    resident_bytes = sum(t.numel() * 8 for pair in sets for t in pair) + sum(k.numel() * 8 for k in keys)
+    resident_bytes = (sum(t.numel() * 8 for pair in sets for t in pair) + sum(k.numel() * 8 for k in keys)
+                      + sum(c.numel() * 8 for c in cts))
 
     rows = ["ntt_forward", "poly_mul_ntt", "ct_tensor_ntt", "ntt_inverse", "automorph", "keyswitch"]
     ev = {r: [] for r in rows}
@@ -433,18 +599,20 @@ def main():
         run("poly_mul_ntt", lambda: B.poly_mul_ntt(plan, C, a, b))
         run("ct_tensor_ntt", lambda: B.ct_tensor_ntt(plan, D, a, b))
         run("ntt_inverse", lambda: B.ntt_inverse(plan, C))
-        run("automorph", lambda: B.automorph(plan, E, C, g, 0))
+        # the B operand of the next set: last touched a whole step (> 1 GB of traffic) ago
+        run("automorph", lambda: B.automorph(plan, E, sets[(s + 1) % len(sets)][1], g, 0))
         if ksp is not None:
-            run("keyswitch", lambda: B.keyswitch(ksp, ks_out, ct, keys[s % len(keys)], g, ws))
+            run("keyswitch", lambda: B.keyswitch(ksp, ks_out, cts[s % len(cts)], keys[s % len(keys)], g, ws))
 
     for s in range(args.warmup):
         step(s, False)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(args.warmup + s, True)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with ClockSampler() as clock:
+        t0 = time.perf_counter()
+        for s in range(args.steps):
+            step(args.warmup + s, True)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
 
     ms = {r: [e0.elapsed_time(e1) for e0, e1 in ev[r]] for r in rows if ev[r]}
     mean_ms = {r: sum(v) / len(v) for r, v in ms.items()}
@@ -481,19 +649,34 @@ def main():
     alu_tops = butterflies * MUL32_PER_BUTTERFLY / fwd_s / 1e12
     fwd_gbps = alg_bytes["ntt_forward"] / fwd_s / 1e9
     traffic = recorded_traffic()
+    kname = "ntt_forward (ntt_col_kernel + ntt_row_kernel, n=2^16, 384 limbs)"
     roofline = {
-        "kernel": "ntt_forward (ntt_col_kernel + ntt_row_kernel, n=2^16, 384 limbs)",
-        "bound": "alu",
+        "kernel": kname,
+        "bound": "hbm",
+        "achieved": round(fwd_gbps, 1),
+        "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": round(fwd_gbps / HBM_PEAK_GBPS, 4),
+        "traffic": traffic,
+        "bytes": "16 n per limb-NTT (each residue read and written once) x 384 limb-NTTs per call",
+        "us_per_call": round(fwd_s * 1e6, 2),
+        "limiter": "VALU issue, not HBM (alu_issue)",
+    }
+    clk = clock.summary()
+    alu_issue = {
+        "kernel": kname,
         "achieved": round(alu_tops, 3),
         "peak": round(MUL32_PEAK_TOPS, 2),
         "unit": "TOP/s",
         "frac": round(alu_tops / MUL32_PEAK_TOPS, 4),
-        "traffic": traffic,
         "ops": "32-bit multiplies, 10 per 64-bit Shoup butterfly",
-        "hbm_alg_GBps": round(fwd_gbps, 1),
-        "hbm_frac": round(fwd_gbps / HBM_PEAK_GBPS, 4),
-        "us_per_call": round(fwd_s * 1e6, 2),
+        "peak_assumes": "256 CUs x 64 lanes x 2400 MHz, one 32-bit multiply per lane per clock",
+        "sampled_sclk": clk,
     }
+    if clk.get("median_MHz"):
+        alu_issue["frac_at_sampled_median_sclk"] = round(alu_tops / (256 * 64 * clk["median_MHz"] * 1e6 / 1e12), 4)
+    valu = recorded_valu()
+    alu_issue["counters"] = valu
     rt_ms = mean_ms["ntt_forward"] + mean_ms["ntt_inverse"]
     out = {
         "metric": "limb-NTTs/sec + achieved HBM GB/s (N=2^16, 60-bit, 1 GPU); keyswitches/sec",
@@ -515,13 +698,15 @@ def main():
         "keyswitches_per_s": per_row.get("keyswitch", {}).get("keyswitch_per_s"),
         "rows": per_row,
         "roofline": roofline,
+        "alu_issue": alu_issue,
         "input_gen_s": round(gen_s, 2),
     }
     out["device"] = device_info()
+    out["galois"] = galois_rows(B, plan, sets, E, galois, args.next_reps)
     if not args.no_next_rows:
         out["next_rows"] = next_rows(B, plan, ksp, ws, primes, W, KS, C, ct, ksk0, galois, args.next_reps)
     if not args.no_other_configs:
-        del sets, keys, C, E, D
+        del sets, keys, cts, C, E, D
         out["other_configs"] = other_configs(B, args.next_reps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(primes, n, nq, npr, dnum, args.cpu_sample_limbs, a_host, b_host,
