@@ -254,6 +254,21 @@ int keyswitch_workspace_size(const ntt_ks_plan *plan, uint64_t batch, size_t *by
 int keyswitch(const ntt_ks_plan *plan, uint64_t *out, const uint64_t *ct, const uint64_t *ksk,
               uint64_t galois_elt, uint64_t batch, void *workspace, size_t workspace_bytes, void *stream);
 
+/* keyswitch() for callers that cannot allocate device memory on the call path
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation, arguments, layouts and errors as keyswitch(),
+ * with the workspace taken from a static device array of the library instead of a
+ * caller buffer.  The array holds 80 MiB (83,886,080 bytes) per GPU -- one
+ * ciphertext at n = 2^16 over 24 + 8 primes with 3 digits -- and a call whose
+ * keyswitch_workspace_size exceeds it returns NTT_EUNSUPPORTED with nothing
+ * launched.  A GPU holds the array from the first call on it until the process
+ * ends.  Every call on one GPU uses that GPU's one array: calls that overlap on a
+ * GPU (concurrent streams, or threads) race on it and must be ordered by the
+ * caller.  Nothing needs to start at zero: each call writes every workspace byte
+ * it reads.  Allocates nothing and never synchronises (debug checks aside). */
+int keyswitch_noalloc(const ntt_ks_plan *plan, uint64_t *out, const uint64_t *ct, const uint64_t *ksk,
+                      uint64_t galois_elt, uint64_t batch, void *stream);
+
 /* Bytes of device workspace keyswitch_hoisted needs for num_rot rotations of `batch`
  * ciphertexts: batch * (dnum + 2 num_rot) * (num_q + num_p) * n * 8 (caller-owned,
  * as for keyswitch_workspace_size).  NTT_EINVAL for num_rot 0, NTT_EUNSUPPORTED for

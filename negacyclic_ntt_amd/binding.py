@@ -53,6 +53,7 @@ def lib():
             "keyswitch_plan_create": (i32, [ctypes.POINTER(_VP), _VP, u32, u32, u32]),
             "keyswitch_workspace_size": (i32, [_VP, u64, ctypes.POINTER(sz)]),
             "keyswitch": (i32, [_VP, _VP, _VP, _VP, u64, u64, _VP, sz, _VP]),
+            "keyswitch_noalloc": (i32, [_VP, _VP, _VP, _VP, u64, u64, _VP]),
             "keyswitch_plan_destroy": (None, [_VP]),
             "relinearize": (i32, [_VP, _VP, _VP, _VP, u64, _VP, sz, _VP]),
             "modraise_plan_create": (i32, [ctypes.POINTER(_VP), _VP, u32, u32]),
@@ -333,6 +334,22 @@ def keyswitch(ks: KeySwitchPlan, out, ct, ksk, galois_elt: int, ws=None, stream=
     _check(lib().keyswitch(ks.handle, _VP(out.data_ptr()), _VP(ct.data_ptr()), _VP(ksk.data_ptr()), galois_elt,
                            batch, _VP(ws.data_ptr()), ws.numel() * ws.element_size(), _stream_ptr(ct, stream)),
            "keyswitch")
+    return out
+
+
+def keyswitch_noalloc(ks: KeySwitchPlan, out, ct, ksk, galois_elt: int, stream=None):
+    """keyswitch() with the library's static device workspace (allocates nothing; see
+    keyswitch_noalloc in the header for its size limit and sharing rule)."""
+    plan = ks.qp_plan
+    batch, limbs = _check_tensor(ct, plan, "ct", lead=1)
+    _check_tensor(out, plan, "out", lead=1)
+    _check_tensor(ksk, plan, "ksk", lead=1)
+    if limbs != ks.num_q or ct.shape[-3] != 2 or out.shape != ct.shape:
+        raise ValueError("ct/out must be [batch, 2, num_q, n]")
+    if tuple(ksk.shape) != (ks.dnum, 2, ks.num_q + ks.num_p, plan.n):
+        raise ValueError("ksk must be [dnum, 2, num_q + num_p, n]")
+    _check(lib().keyswitch_noalloc(ks.handle, _VP(out.data_ptr()), _VP(ct.data_ptr()), _VP(ksk.data_ptr()),
+                                   galois_elt, batch, _stream_ptr(ct, stream)), "keyswitch_noalloc")
     return out
 
 

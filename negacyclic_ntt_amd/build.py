@@ -13,7 +13,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libnegacyclic_ntt.so")
-SOURCES = ["plan.cpp", "capi.cpp", "ntt.hip", "elementwise.hip", "keyswitch.hip"]
+SOURCES = ["plan.cpp", "capi.cpp", "ntt.hip", "elementwise.hip", "keyswitch.hip", "noalloc.hip"]
 ARCH = "gfx950"
 FLAGS = [
     "-O3", f"--offload-arch={ARCH}", "-std=c++17", "-fPIC", "-Wall",

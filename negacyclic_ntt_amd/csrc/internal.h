@@ -150,6 +150,9 @@ bool range_is_narrow(const ntt_plan* p, uint32_t limb_begin, uint32_t num_limbs)
 // True when every prime in the range is below 2^60.
 bool range_below60(const ntt_plan* p, uint32_t limb_begin, uint32_t num_limbs);
 
+// HIP device of a key-switch plan (keyswitch.hip).
+int ks_plan_device(const ntt_ks_plan* p);
+
 // Element-wise launchers (elementwise.hip).
 hipError_t launch_pointwise(const ntt_plan* p, uint64_t* out, const uint64_t* a, const uint64_t* b, uint64_t batch,
                             uint32_t limb_begin, uint32_t num_limbs, hipStream_t s);

@@ -662,6 +662,8 @@ extern "C" int keyswitch_plan_create(ntt_ks_plan** out, const ntt_plan* qp, uint
   return NTT_OK;
 }
 
+int nntt::ks_plan_device(const ntt_ks_plan* p) { return p->qp->device; }
+
 static uint64_t ws_elems(const ntt_ks_plan* p, uint64_t batch) {
   return batch * (uint64_t)(p->dnum + 2) * (p->nq + p->np) * p->qp->n;
 }
