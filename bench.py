@@ -357,13 +357,21 @@ def other_configs(B, reps):
     f_graph_ms = time_graph(fwd)
     t_ms = time_cycle([lambda x=x, y=y: B.ct_tensor_ntt(plan, d, x, y) for x, y in copies], max(reps, len(copies)))
     i_ms = time_cycle([lambda: B.ntt_inverse(plan, d)], reps)
+    # the whole chain (NTT of both operands, tensor, INTT of the three outputs) in one launch
+    prod = [lambda x=x, y=y: B.ct_tensor_coeff(plan, d, x, y) for x, y in copies]
+    c_ms = time_cycle(prod, max(reps, len(copies)))
+    c_graph_ms = time_graph(prod)
     out[W.name] = {"ntt_forward_us": r3(f_ms * 1e3), "ntt_forward_graph_us": r3(f_graph_ms * 1e3),
                    "ntt_forward_limb_ntt_per_s": round(limbs / (f_ms * 1e-3)),
                    "ntt_forward_graph_limb_ntt_per_s": round(limbs / (f_graph_ms * 1e-3)),
                    "ct_tensor_us": r3(t_ms * 1e3),
                    "ct_tensor_alg_GBps": round(56 * (a.numel() // 2) / (t_ms * 1e-3) / 1e9, 1),
                    "ntt_inverse_of_tensor_us": r3(i_ms * 1e3),
-                   "ntt_inverse_limb_ntt_per_s": round(d.numel() // W.n / (i_ms * 1e-3))}
+                   "ntt_inverse_limb_ntt_per_s": round(d.numel() // W.n / (i_ms * 1e-3)),
+                   "chain_4_launches_us": r3((2 * f_ms + t_ms + i_ms) * 1e3),
+                   "ct_tensor_coeff_us": r3(c_ms * 1e3), "ct_tensor_coeff_graph_us": r3(c_graph_ms * 1e3),
+                   "ct_tensor_coeff_alg_GBps": round(56 * (a.numel() // 2) / (c_ms * 1e-3) / 1e9, 1),
+                   "ct_tensor_coeff_limb_transforms_per_s": round(7 * (a.numel() // 2) // W.n / (c_ms * 1e-3))}
     del copies, a, b, d, plan
 
     W = workloads.POLYMUL  # n = 2048, 4 x 30-bit: NTT(A), NTT(B), pointwise, INTT

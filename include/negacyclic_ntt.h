@@ -162,6 +162,19 @@ int poly_mul_ntt(const ntt_plan *plan, uint64_t *out, const uint64_t *a, const u
 int ct_tensor_ntt(const ntt_plan *plan, uint64_t *out, const uint64_t *a, const uint64_t *b, uint64_t batch,
                   uint32_t limb_begin, uint32_t num_limbs, void *stream);
 
+/* Ciphertext product in the coefficient domain, for n <= 4096: a, b are
+ * [batch][2][num_limbs][n] coefficient-domain ciphertexts; out is
+ * [batch][3][num_limbs][n] with the negacyclic products (in Z_q[X]/(X^n + 1))
+ *   d0 = a0 b0,  d1 = a0 b1 + a1 b0,  d2 = a1 b1,
+ * i.e. INTT(ct_tensor_ntt(NTT(a), NTT(b))), computed in one launch that keeps each
+ * (ciphertext, limb) in LDS through the four forward transforms, the slot products
+ * and the three inverse transforms.  This is the ciphertext "mul" of the kestrel-llm
+ * CKKS layer (section 3) on its inner-chain shape (section 5: n = 2048, 112 primes,
+ * 4 token positions x 2 components).  out must not overlap a or b (NTT_EOVERLAP);
+ * n > 4096 is NTT_EUNSUPPORTED (use ntt_forward, ct_tensor_ntt, ntt_inverse). */
+int ct_tensor_coeff(const ntt_plan *plan, uint64_t *out, const uint64_t *a, const uint64_t *b, uint64_t batch,
+                    uint32_t limb_begin, uint32_t num_limbs, void *stream);
+
 /* Galois automorphism sigma_g: X -> X^g, galois_elt odd and < 2n.
  * domain 0 (coefficient): out[i*g mod 2n] = in[i] when i*g mod 2n < n, else
  *   out[i*g mod 2n - n] = -in[i] (a signed permutation).

@@ -49,6 +49,7 @@ def lib():
             "ntt_forward_galois": (i32, [_VP, _VP, _VP, u64, u64, u32, u32, _VP]),
             "poly_mul_ntt": (i32, [_VP, _VP, _VP, _VP, u64, u32, u32, _VP]),
             "ct_tensor_ntt": (i32, [_VP, _VP, _VP, _VP, u64, u32, u32, _VP]),
+            "ct_tensor_coeff": (i32, [_VP, _VP, _VP, _VP, u64, u32, u32, _VP]),
             "automorph": (i32, [_VP, _VP, _VP, u64, i32, u64, u32, u32, _VP]),
             "keyswitch_plan_create": (i32, [ctypes.POINTER(_VP), _VP, u32, u32, u32]),
             "keyswitch_workspace_size": (i32, [_VP, u64, ctypes.POINTER(sz)]),
@@ -229,6 +230,19 @@ def ct_tensor_ntt(plan: Plan, out, a, b, limb_begin: int = 0, stream=None):
         raise ValueError("expected a, b [..., 2, L, n] and out [..., 3, L, n]")
     _check(lib().ct_tensor_ntt(plan.handle, _VP(out.data_ptr()), _VP(a.data_ptr()), _VP(b.data_ptr()), batch,
                                limb_begin, limbs, _stream_ptr(a, stream)), "ct_tensor_ntt")
+    return out
+
+
+def ct_tensor_coeff(plan: Plan, out, a, b, limb_begin: int = 0, stream=None):
+    """Coefficient-domain ciphertext product: a, b [..., 2, limbs, n] -> out [..., 3, limbs, n]
+    (negacyclic products d0 = a0 b0, d1 = a0 b1 + a1 b0, d2 = a1 b1; n <= 4096)."""
+    batch, limbs = _check_tensor(a, plan, "a", lead=1)
+    _check_tensor(b, plan, "b", lead=1)
+    _check_tensor(out, plan, "out", lead=1)
+    if a.shape != b.shape or a.shape[-3] != 2 or out.shape[:-3] != a.shape[:-3] or out.shape[-3:] != (3, limbs, plan.n):
+        raise ValueError("expected a, b [..., 2, L, n] and out [..., 3, L, n]")
+    _check(lib().ct_tensor_coeff(plan.handle, _VP(out.data_ptr()), _VP(a.data_ptr()), _VP(b.data_ptr()), batch,
+                                 limb_begin, limbs, _stream_ptr(a, stream)), "ct_tensor_coeff")
     return out
 
 

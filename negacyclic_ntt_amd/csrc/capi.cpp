@@ -176,6 +176,23 @@ extern "C" int ct_tensor_ntt(const ntt_plan* p, uint64_t* out, const uint64_t* a
   return status_of(launch_tensor(p, out, a, b, batch, limb_begin, num_limbs, (hipStream_t)stream));
 }
 
+extern "C" int ct_tensor_coeff(const ntt_plan* p, uint64_t* out, const uint64_t* a, const uint64_t* b,
+                               uint64_t batch, uint32_t limb_begin, uint32_t num_limbs, void* stream) {
+  uint64_t elems = 0;
+  int rc = check_plan_range(p, batch, limb_begin, num_limbs, 3, &elems);
+  if (rc) return rc;
+  if (!chain_supported(p)) return NTT_EUNSUPPORTED;
+  if (!elems) return NTT_OK;
+  if (!out || !a || !b || !aligned16(out) || !aligned16(a) || !aligned16(b)) return NTT_EINVAL;
+  const uint64_t in_bytes = elems / 3 * 2 * 8, out_bytes = elems * 8;
+  if (overlaps(out, out_bytes, a, in_bytes) || overlaps(out, out_bytes, b, in_bytes)) return NTT_EOVERLAP;
+  if ((rc = debug_check_inputs(p, a, 2 * batch, limb_begin, num_limbs, (hipStream_t)stream))) return rc;
+  if ((rc = debug_check_inputs(p, b, 2 * batch, limb_begin, num_limbs, (hipStream_t)stream))) return rc;
+  DeviceGuard g(p->device);
+  if (!g.ok) return NTT_EDEVICE;
+  return status_of(launch_ct_tensor_coeff(p, out, a, b, batch, limb_begin, num_limbs, (hipStream_t)stream));
+}
+
 extern "C" int automorph(const ntt_plan* p, uint64_t* out, const uint64_t* in, uint64_t galois_elt, int domain,
                          uint64_t batch, uint32_t limb_begin, uint32_t num_limbs, void* stream) {
   uint64_t elems = 0;

@@ -140,6 +140,14 @@ hipError_t launch_ntt_galois(const ntt_plan* p, uint64_t* out, const uint64_t* i
 bool intt_mac_supported(const ntt_plan* p);
 hipError_t launch_intt_mac(const ntt_plan* p, uint64_t* acc, const uint64_t* ext, const uint64_t* ksk, uint64_t batch,
                            uint32_t nqp, uint32_t dnum, uint32_t chunk, hipStream_t s);
+// The whole middle of a key-switch for the two-pass sizes (n >= 2^15, 1 <= dnum <= 4 and
+// one reduction for the dnum products, chunk >= dnum): forward NTT of the digits ext
+// [batch][dnum][nqp][n] (Montgomery form; overwritten), key product and inverse NTT
+// into acc [batch][2][nqp][n].  The NTT-domain digits stay in LDS between the forward
+// row pass and the key product.
+bool ks_middle_supported(const ntt_plan* p, uint32_t dnum, uint32_t chunk);
+hipError_t launch_ks_middle(const ntt_plan* p, uint64_t* acc, uint64_t* ext, const uint64_t* ksk, uint64_t batch,
+                            uint32_t nqp, uint32_t dnum, hipStream_t s);
 // The same for hoisted rotations: acc [num_rot][batch][2][nqp][n] from the shared digits
 // gathered through each rotation's slot permutation, keys [num_rot][dnum][2][nqp][n].
 hipError_t launch_intt_mac_hoisted(const ntt_plan* p, uint64_t* acc, const uint64_t* ext, const uint64_t* ksk,
@@ -149,6 +157,12 @@ hipError_t launch_intt_mac_hoisted(const ntt_plan* p, uint64_t* acc, const uint6
 bool range_is_narrow(const ntt_plan* p, uint32_t limb_begin, uint32_t num_limbs);
 // True when every prime in the range is below 2^60.
 bool range_below60(const ntt_plan* p, uint32_t limb_begin, uint32_t num_limbs);
+
+// Coefficient-domain ciphertext product (ntt.hip), n <= 2^12: out [batch][3][L][n] =
+// INTT(tensor(NTT(a), NTT(b))) for a, b [batch][2][L][n], one launch.
+bool chain_supported(const ntt_plan* p);
+hipError_t launch_ct_tensor_coeff(const ntt_plan* p, uint64_t* out, const uint64_t* a, const uint64_t* b,
+                                  uint64_t batch, uint32_t limb_begin, uint32_t num_limbs, hipStream_t s);
 
 // HIP device of a key-switch plan (keyswitch.hip).
 int ks_plan_device(const ntt_ks_plan* p);

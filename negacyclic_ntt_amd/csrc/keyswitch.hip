@@ -11,8 +11,12 @@
 //      section 4.2) and reduced onto every prime of Q u P;
 //   3. forward NTT of every extended digit;
 //   4. key inner product acc_c = sum_j NTT(D_j) * ksk[j][c] (FHElium's key-switch
-//      multiply-accumulate) -- for n >= 2^15 computed inside the first pass of
-//   5. the inverse NTT of both accumulators (ntt.hip), else by mac_kernel;
+//      multiply-accumulate);
+//   5. the inverse NTT of both accumulators.  For n >= 2^15 with up to 4 digits, one
+//      kernel per row tile runs the forward row pass of every digit, the key product
+//      and the inverse row pass (ntt.hip, ntt_row_ks_kernel), between the two column
+//      passes; with more digits the key product rides on the inverse's row pass;
+//      smaller rings use mac_kernel between whole-row transforms;
 //   6. ModDown (exact floor, FHElium's "QP-to-Q ModDown"):
 //      out_c = floor(X_c / P) mod q_l = (acc_c[l] - (X_c mod P)) * P^-1 mod q_l,
 //      X_c mod P from the P residues by Garner; out_0 += sigma_g(c0).
@@ -818,6 +822,12 @@ int ks_run(const ntt_ks_plan* p, uint64_t* out, const KsIo& io, const uint64_t* 
   const uint32_t h = galois_inverse(qp, galois_elt);
   int rc = ks_modup(p, ext, io, h, batch, s);
   if (rc) return rc;
+  if (ks_middle_supported(qp, dnum, p->mac_chunk)) {  // forward NTT, key product, inverse NTT
+    if (launch_ks_middle(qp, acc, ext, ksk, batch, nqp, dnum, s) != hipSuccess) return NTT_EDEVICE;
+    HoistArgs ha{};
+    ha.h[0] = h;
+    return ks_moddown(p, out, acc, io, ha, 1, batch, s);
+  }
   if (launch_ntt(qp, ext, batch * dnum, 0, nqp, false, s) != hipSuccess) return NTT_EDEVICE;
   if (intt_mac_supported(qp)) {  // key product fused into the inverse transform's first pass
     if (launch_intt_mac(qp, acc, ext, ksk, batch, nqp, dnum, p->mac_chunk, s) != hipSuccess) return NTT_EDEVICE;

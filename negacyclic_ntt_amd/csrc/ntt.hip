@@ -21,10 +21,16 @@
 //                     residues fit the 160 KiB LDS of one gfx950 workgroup).
 //   ntt_col_kernel / ntt_row_kernel : the two halves for n = 2^15, 2^16; the
 //                     intermediate goes through L2/MALL/HBM between launches.
+//   ntt_row_ks_kernel : the key-switch's middle for up to 4 digits -- the forward row
+//                     pass of every digit's row tile, the key product of both
+//                     components and the inverse row pass, the digits kept in LDS.
 //   ntt_row_mac_kernel / ntt_row_mac_hoisted_kernel : the inverse transform's first
 //                     (row) pass with the key-switch's key product computed as the
-//                     row tile is loaded (one rotation, or hoisted rotations whose
+//                     row tile is loaded (more digits, or hoisted rotations whose
 //                     digits are gathered through the NTT-domain slot permutation).
+//   ct_tensor_coeff_kernel : the coefficient-domain ciphertext product for n <= 2^12,
+//                     four forward transforms, slot products and three inverse
+//                     transforms of one (ciphertext, limb) in LDS.
 // Inside a workgroup, each thread holds one radix-2^r "set" (up to 16 residues)
 // in registers and runs r stages on it; sets are exchanged through LDS between
 // passes.  LDS rows are padded by one slot per 128 bytes so strided set accesses
@@ -122,10 +128,11 @@ __device__ __forceinline__ void run_pass(typename A::T* lds, int tid, const GetS
   constexpr int SPAN = M >> S0;      // extent of one group at stage S0
   constexpr int SETS = NSUB * SETS_PER_SUB;
   constexpr int STRIDE = sub_stride<A>(LOGM);
-  static_assert(SETS % NT == 0, "sets must divide evenly");
+  constexpr int ITERS = (SETS + NT - 1) / NT;
 #pragma unroll
-  for (int it = 0; it < SETS / NT; ++it) {
+  for (int it = 0; it < ITERS; ++it) {
     const int set = tid + it * NT;
+    if (SETS % NT != 0 && set >= SETS) break;  // a ragged last round: the rest wait at the barrier
     const int sub = set / SETS_PER_SUB, u = set % SETS_PER_SUB;
     const int g = u / TP, r = u % TP;
     const int pos0 = g * SPAN + r;
@@ -386,6 +393,105 @@ __global__ __launch_bounds__(LdsCfg<LOGN>::NT) void ntt_lds_kernel(uint64_t* dat
       v.x = finish<A, FWD>(lds[sub * STRIDE + lpos<A>(pos)], m);
       v.y = finish<A, FWD>(lds[sub * STRIDE + lpos<A>(pos + 1)], m);
       *reinterpret_cast<ulonglong2*>(data + (row0 + sub) * N + pos) = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Ciphertext product in the coefficient domain, n <= 2^12: one block per (ciphertext,
+// limb) holds a0, a1, b0, b1 in LDS, transforms all four, forms
+//   d0 = a0 b0,  d1 = a0 b1 + a1 b0,  d2 = a1 b1   (slot by slot, mod q)
+// and inverse-transforms the three; only the operands and the result cross HBM.
+template <int LOGN>
+struct ChainCfg {
+  static constexpr Sched S = make_sched(LOGN);
+  static constexpr int N = 1 << LOGN;
+  static constexpr int NT0 = 4 * (N >> S.r[0]);  // one radix-2^r0 set per thread over four rows
+  static constexpr int NT = NT0 < 64 ? 64 : (NT0 > 1024 ? 1024 : NT0);
+};
+constexpr uint32_t kChainMaxLogN = 12;
+
+template <class A, int LOGN>
+__global__ __launch_bounds__(ChainCfg<LOGN>::NT) void ct_tensor_coeff_kernel(
+    uint64_t* __restrict__ out, const uint64_t* __restrict__ a, const uint64_t* __restrict__ b,
+    const void* __restrict__ tw_fwd, const void* __restrict__ tw_inv, const ModInfo* __restrict__ mods,
+    uint32_t num_limbs, uint32_t limb_begin, uint64_t batch) {
+  using T = typename A::T;
+  constexpr int N = ChainCfg<LOGN>::N, NT = ChainCfg<LOGN>::NT;
+  constexpr int STRIDE = sub_stride<A>(LOGN);
+  __shared__ T lds[4 * STRIDE];
+  const int tid = threadIdx.x;
+  const Place pl = place_block(1, batch, num_limbs, 0);
+  const uint64_t ct = pl.row / num_limbs;
+  const uint32_t l = pl.limb, limb = limb_begin + l;
+  const uint64_t plane = (uint64_t)num_limbs * N;
+  // row r of the four: a0, a1, b0, b1
+  auto src = [&](int r) { return (r < 2 ? a : b) + (2 * ct + (r & 1)) * plane + (uint64_t)l * N; };
+
+  // rows a0, a1, b0, b1, every load issued before the first LDS write
+  constexpr int kPairs = 2 * N, kLoads = (kPairs + NT - 1) / NT;
+  ulonglong2 buf[kLoads];
+#pragma unroll
+  for (int it = 0; it < kLoads; ++it) {
+    const int e = 2 * (tid + it * NT);
+    if (kPairs % NT == 0 || e < 4 * N) buf[it] = *reinterpret_cast<const ulonglong2*>(src(e / N) + e % N);
+  }
+#pragma unroll
+  for (int it = 0; it < kLoads; ++it) {
+    const int e = 2 * (tid + it * NT);
+    if (kPairs % NT == 0 || e < 4 * N) {
+      const int r = e / N, pos = e % N;
+      lds[r * STRIDE + lpos<A>(pos)] = (T)buf[it].x;
+      lds[r * STRIDE + lpos<A>(pos + 1)] = (T)buf[it].y;
+    }
+  }
+  __syncthreads();
+
+  const ModInfo& m = mods[limb];
+  const T q = modulus<A>(m);
+  {
+    const typename A::Tw* tw = table_of<A>(tw_fwd, limb, N);
+    auto get_sub = [&](int) {
+      SubParams<A> sp;
+      sp.tw = tw;
+      sp.q = q;
+      sp.prefix = 1;
+      return sp;
+    };
+    run_passes<A, true, LOGN, 4, NT, 0, decltype(get_sub), 0, false, true>(lds, tid, get_sub);
+  }
+  // d0, d1, d2 over rows 0, 1, 2: each thread reads and writes only its own slots
+  const Barrett br = m.br;
+  for (int k = tid; k < N; k += NT) {
+    const int o = lpos<A>(k);
+    const uint64_t x0 = finish<A, true>(lds[o], m), x1 = finish<A, true>(lds[STRIDE + o], m);
+    const uint64_t y0 = finish<A, true>(lds[2 * STRIDE + o], m), y1 = finish<A, true>(lds[3 * STRIDE + o], m);
+    lds[o] = (T)barrett_mul(x0, y0, br);
+    lds[STRIDE + o] = (T)add_mod(barrett_mul(x0, y1, br), barrett_mul(x1, y0, br), br.q);
+    lds[2 * STRIDE + o] = (T)barrett_mul(x1, y1, br);
+  }
+  __syncthreads();
+  {
+    const typename A::Tw* tw = table_of<A>(tw_inv, limb, N);
+    auto get_sub = [&](int) {
+      SubParams<A> sp;
+      sp.tw = tw;
+      sp.q = q;
+      sp.prefix = 1;
+      return sp;
+    };
+    run_passes<A, false, LOGN, 3, NT, 0, decltype(get_sub), 0, false, true>(lds, tid, get_sub);
+  }
+  constexpr int kOutPairs = 3 * N / 2, kStores = (kOutPairs + NT - 1) / NT;
+#pragma unroll
+  for (int it = 0; it < kStores; ++it) {
+    const int e = 2 * (tid + it * NT);
+    if (kOutPairs % NT == 0 || e < 3 * N) {
+      const int r = e / N, pos = e % N;
+      ulonglong2 v;
+      v.x = finish<A, false>(lds[r * STRIDE + lpos<A>(pos)], m);
+      v.y = finish<A, false>(lds[r * STRIDE + lpos<A>(pos + 1)], m);
+      *reinterpret_cast<ulonglong2*>(out + (3 * ct + r) * plane + (uint64_t)l * N + pos) = v;
     }
   }
 }
@@ -693,6 +799,143 @@ __global__ __launch_bounds__(RowCfg<LOGN2>::NT) void ntt_row_mac_kernel(uint64_t
   }
 }
 
+// The middle of a key-switch for n = N1 x 2^8 in one block per (ciphertext b, limb t,
+// tile of ROWS rows): the forward transform's row pass of every digit's tile (the digits
+// come from the forward column pass, [batch][DN][nqp][n]), the key product of both
+// components,
+//   acc_c = sum_j NTT(ext_j)[t] * ksk[j][c][t]   (mod q_t),
+// and the inverse transform's row pass of both accumulators, which are stored as the
+// intermediate of the inverse ([batch][2][nqp][n]) for its column pass.  The
+// NTT-domain digits never leave LDS.  The digits carry the factor 2^64 of ModUp's
+// Montgomery form, so the exact 128-bit sum of the DN products (DN q^2 < q 2^64 for
+// DN <= 4 and q < 2^62) is reduced once by Montgomery to the plain residue.
+template <int DN>
+constexpr int ks_tiles() {
+  return DN > 2 ? DN : 2;  // LDS tiles: the DN digit tiles, reused for the two accumulators
+}
+template <int DN, int ROWS>
+constexpr int ks_threads() {
+  return 16 * ROWS * ks_tiles<DN>();  // one radix-16 set of a 2^8 row per thread and pass
+}
+
+template <class A, int LOGN1, int DN, int ROWS>
+__global__ __launch_bounds__((ks_threads<DN, ROWS>())) void ntt_row_ks_kernel(
+    uint64_t* __restrict__ acc, const uint64_t* __restrict__ ext, const uint64_t* __restrict__ ksk,
+    const void* __restrict__ tw_fwd, const void* __restrict__ tw_inv, const ModInfo* __restrict__ mods, uint32_t nqp,
+    uint64_t batch) {
+  using T = typename A::T;
+  constexpr int LOGN2 = 8;
+  constexpr int N1 = 1 << LOGN1, N2 = 1 << LOGN2, N = N1 * N2;
+  constexpr int TILES = ks_tiles<DN>(), NT = ks_threads<DN, ROWS>();
+  constexpr int STRIDE = sub_stride<A>(LOGN2);
+  constexpr int TILE = ROWS * N2;  // residues of one tile
+  __shared__ T lds[TILES * ROWS * STRIDE];
+  const int tid = threadIdx.x;
+  const Place pl = place_block(N1 / ROWS, batch, nqp, 0);
+  const uint64_t b = pl.row / nqp;
+  const uint32_t t = pl.limb;
+  const int r0 = (int)pl.tile * ROWS;
+  const size_t off = (size_t)r0 * N2;  // first element of the tile in the limb
+  const uint64_t plane = (uint64_t)nqp * N;
+  const uint64_t* xe = ext + (b * DN * nqp + t) * (uint64_t)N + off;  // digit j at + j plane
+  const uint64_t* kk = ksk + (uint64_t)t * N + off;                   // key (j, c) at + (2 j + c) plane
+  uint64_t* ao = acc + (b * 2 * nqp + t) * (uint64_t)N + off;          // component c at + c plane
+
+  // Digit tiles, every load issued before the first LDS write.
+  constexpr int kLoads = (DN * TILE + 2 * NT - 1) / (2 * NT);
+  ulonglong2 buf[kLoads];
+#pragma unroll
+  for (int it = 0; it < kLoads; ++it) {
+    const int e = 2 * tid + it * 2 * NT;
+    if (e < DN * TILE) buf[it] = *reinterpret_cast<const ulonglong2*>(xe + (e / TILE) * plane + e % TILE);
+  }
+#pragma unroll
+  for (int it = 0; it < kLoads; ++it) {
+    const int e = 2 * tid + it * 2 * NT;
+    if (e < DN * TILE) {
+      const int sub = e / N2, pos = e % N2;  // sub = j ROWS + row within the tile
+      lds[sub * STRIDE + lpos<A>(pos)] = (T)buf[it].x;
+      lds[sub * STRIDE + lpos<A>(pos + 1)] = (T)buf[it].y;
+    }
+  }
+  __syncthreads();
+
+  const ModInfo& m = mods[t];
+  const T qt = modulus<A>(m);
+  constexpr bool kPerm = row_tw_permuted(LOGN1 + LOGN2);
+  {
+    const typename A::Tw* tw = table_of<A>(tw_fwd, t, N);
+    auto get_sub = [&](int sub) {
+      SubParams<A> sp;
+      sp.tw = tw;
+      sp.q = qt;
+      sp.prefix = (uint32_t)N1 + (uint32_t)(r0 + sub % ROWS);
+      return sp;
+    };
+    run_passes<A, true, LOGN2, DN * ROWS, NT, 0, decltype(get_sub), 1, false, false, kPerm>(lds, tid, get_sub);
+  }
+
+  // Key product: each thread reads its own element pairs of every digit tile and writes
+  // the two accumulators to the same positions of tiles 0 and 1 (no other thread
+  // touches those positions, so no barrier is needed between the reads and writes).
+  const uint64_t q = m.q, ninv = m.mont_ninv;
+#pragma unroll 2
+  for (int p = tid; p < TILE / 2; p += NT) {
+    const int e = 2 * p;
+    const int row = e / N2, pos = e % N2;
+    ulonglong2 k0[DN], k1[DN];
+#pragma unroll
+    for (int j = 0; j < DN; ++j) {
+      k0[j] = load_key(kk + (2 * j) * plane + e);
+      k1[j] = load_key(kk + (2 * j + 1) * plane + e);
+    }
+    Acc128 s0x{0, 0}, s0y{0, 0}, s1x{0, 0}, s1y{0, 0};
+#pragma unroll
+    for (int j = 0; j < DN; ++j) {
+      T* d = lds + (j * ROWS + row) * STRIDE;
+      const uint64_t dx = finish<A, true>(d[lpos<A>(pos)], m);  // canonical NTT-domain digit
+      const uint64_t dy = finish<A, true>(d[lpos<A>(pos + 1)], m);
+      mac128(s0x, dx, k0[j].x);
+      mac128(s0y, dy, k0[j].y);
+      mac128(s1x, dx, k1[j].x);
+      mac128(s1y, dy, k1[j].y);
+    }
+    T* a0 = lds + row * STRIDE;
+    T* a1 = lds + (ROWS + row) * STRIDE;
+    a0[lpos<A>(pos)] = (T)csub(redc(s0x, q, ninv), q);
+    a0[lpos<A>(pos + 1)] = (T)csub(redc(s0y, q, ninv), q);
+    a1[lpos<A>(pos)] = (T)csub(redc(s1x, q, ninv), q);
+    a1[lpos<A>(pos + 1)] = (T)csub(redc(s1y, q, ninv), q);
+  }
+  __syncthreads();
+
+  {
+    const typename A::Tw* tw = table_of<A>(tw_inv, t, N);
+    auto get_sub = [&](int sub) {
+      SubParams<A> sp;
+      sp.tw = tw;
+      sp.q = qt;
+      sp.prefix = (uint32_t)N1 + (uint32_t)(r0 + sub % ROWS);
+      return sp;
+    };
+    run_passes<A, false, LOGN2, 2 * ROWS, NT, 0, decltype(get_sub), -1, false, true, kPerm>(lds, tid, get_sub);
+  }
+
+  // Both accumulator tiles, unreduced (the inverse column pass finishes them).
+  constexpr int kStores = (2 * TILE + 2 * NT - 1) / (2 * NT);
+#pragma unroll
+  for (int it = 0; it < kStores; ++it) {
+    const int e = 2 * tid + it * 2 * NT;
+    if (e < 2 * TILE) {
+      const int sub = e / N2, pos = e % N2;  // sub = c ROWS + row
+      ulonglong2 v;
+      v.x = A::widen(lds[sub * STRIDE + lpos<A>(pos)]);
+      v.y = A::widen(lds[sub * STRIDE + lpos<A>(pos + 1)]);
+      *reinterpret_cast<ulonglong2*>(ao + (e / TILE) * plane + e % TILE) = v;
+    }
+  }
+}
+
 // Hoisted rotations: accumulator row poly * nqp + t, poly = (r * batch + b) * 2 + c, is
 //   sum_j ext[b][j][t][slot_{g_r}(k)] * ksk[r][j][c][t][k]   (mod q_t)
 // for each slot k of the row tile.  A row tile is an aligned segment of slots, so the
@@ -907,6 +1150,66 @@ hipError_t launch_mac_any(const ntt_plan* p, uint64_t* acc, const MacSrc& ms, ui
   return hipErrorNotSupported;
 }
 
+// The middle of a key-switch for the two-pass sizes: the forward column pass over the
+// digits ext [batch][DN][nqp][n] (in place), ntt_row_ks_kernel into acc
+// [batch][2][nqp][n], and the inverse column pass over acc.  Batches go in parts that
+// keep each launch within the launch cap.
+// Rows per fused tile, measured on MI355X (one key-switch at n = 2^16, 24 + 8 primes,
+// 3 digits): 4 rows 200 us, 8 rows 207-212 us; on-demand twiddles instead of requesting
+// a set's twiddles up front: 208 and 211 us.
+constexpr int kKsRows = 4;
+template <class A, int LOGN1, int DN>
+hipError_t launch_ks_middle_split(const ntt_plan* p, uint64_t* acc, uint64_t* ext, const uint64_t* ksk,
+                                  uint64_t batch, uint32_t nqp, hipStream_t s) {
+  constexpr int LOGN2 = 8;
+  constexpr uint32_t kColBlocks = (1u << LOGN2) / kCols, kRowBlocks = (1u << LOGN1) / kKsRows;
+  constexpr uint32_t kColNT = ColCfg<LOGN1>::NT, kKsNT = ks_threads<DN, kKsRows>();
+  const void* twf = tables_for<A>(p, Op::kForward);
+  const void* twi = tables_for<A>(p, Op::kInverse);
+  const uint64_t N = 1ull << (LOGN1 + LOGN2);
+  const uint64_t per_ct = std::max<uint64_t>({(uint64_t)DN * nqp * kColBlocks * kColNT,
+                                              (uint64_t)nqp * kRowBlocks * kKsNT,
+                                              2ull * nqp * kColBlocks * kColNT});
+  const uint64_t per = items_per_launch(per_ct);
+  if (per == 0) return hipErrorNotSupported;
+  for (uint64_t b0 = 0; b0 < batch; b0 += per) {
+    const uint64_t nb = std::min(per, batch - b0);
+    uint64_t* e = ext + b0 * DN * nqp * N;
+    uint64_t* a = acc + b0 * 2 * nqp * N;
+    hipLaunchKernelGGL((ntt_col_kernel<A, LOGN1, LOGN2, true, false, false>),
+                       dim3((uint32_t)(nb * DN * nqp * kColBlocks)), dim3(kColNT), 0, s, e, e, twf, p->d_mods, nqp,
+                       0u, nb * DN, 1u);
+    hipLaunchKernelGGL((ntt_row_ks_kernel<A, LOGN1, DN, kKsRows>), dim3((uint32_t)(nb * nqp * kRowBlocks)),
+                       dim3(kKsNT), 0, s, a, e, ksk, twf, twi, p->d_mods, nqp, nb);
+    hipLaunchKernelGGL((ntt_col_kernel<A, LOGN1, LOGN2, false, true, false>),
+                       dim3((uint32_t)(nb * 2 * nqp * kColBlocks)), dim3(kColNT), 0, s, a, a, twi, p->d_mods, nqp,
+                       0u, nb * 2, 1u);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+template <class A, int LOGN1>
+hipError_t launch_ks_middle_dn(const ntt_plan* p, uint64_t* acc, uint64_t* ext, const uint64_t* ksk, uint64_t batch,
+                               uint32_t nqp, uint32_t dnum, hipStream_t s) {
+  switch (dnum) {
+    case 1: return launch_ks_middle_split<A, LOGN1, 1>(p, acc, ext, ksk, batch, nqp, s);
+    case 2: return launch_ks_middle_split<A, LOGN1, 2>(p, acc, ext, ksk, batch, nqp, s);
+    case 3: return launch_ks_middle_split<A, LOGN1, 3>(p, acc, ext, ksk, batch, nqp, s);
+    case 4: return launch_ks_middle_split<A, LOGN1, 4>(p, acc, ext, ksk, batch, nqp, s);
+    default: return hipErrorNotSupported;
+  }
+}
+
+template <class A>
+hipError_t launch_ks_middle_any(const ntt_plan* p, uint64_t* acc, uint64_t* ext, const uint64_t* ksk,
+                                uint64_t batch, uint32_t nqp, uint32_t dnum, hipStream_t s) {
+  if (p->logn == 15) return launch_ks_middle_dn<A, 7>(p, acc, ext, ksk, batch, nqp, dnum, s);
+  if (p->logn == 16) return launch_ks_middle_dn<A, 8>(p, acc, ext, ksk, batch, nqp, dnum, s);
+  return hipErrorNotSupported;
+}
+
 template <class A>
 hipError_t launch_any(const ntt_plan* p, uint64_t* data, const uint64_t* in, uint64_t rows, uint32_t limb_begin,
                       uint32_t num_limbs, Op op, uint32_t g, hipStream_t s) {
@@ -935,6 +1238,51 @@ hipError_t launch_any(const ntt_plan* p, uint64_t* data, const uint64_t* in, uin
       return launch_split<A, 8, 8>(p, data, in, rows, limb_begin, num_limbs, op, g, s);
     default:
       return hipErrorInvalidValue;
+  }
+}
+
+template <class A, int LOGN>
+hipError_t launch_chain(const ntt_plan* p, uint64_t* out, const uint64_t* a, const uint64_t* b, uint64_t batch,
+                        uint32_t limb_begin, uint32_t num_limbs, hipStream_t s) {
+  constexpr int NT = ChainCfg<LOGN>::NT;
+  const void* twf = tables_for<A>(p, Op::kForward);
+  const void* twi = tables_for<A>(p, Op::kInverse);
+  const uint64_t per = items_per_launch((uint64_t)num_limbs * NT);  // whole ciphertexts per launch
+  if (per == 0) return hipErrorNotSupported;
+  const uint64_t plane = (uint64_t)num_limbs << LOGN;
+  for (uint64_t c0 = 0; c0 < batch; c0 += per) {
+    const uint64_t nc = std::min(per, batch - c0);
+    hipLaunchKernelGGL((ct_tensor_coeff_kernel<A, LOGN>), dim3((uint32_t)(nc * num_limbs)), dim3(NT), 0, s,
+                       out + c0 * 3 * plane, a + c0 * 2 * plane, b + c0 * 2 * plane, twf, twi, p->d_mods, num_limbs,
+                       limb_begin, nc);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <class A>
+hipError_t launch_chain_any(const ntt_plan* p, uint64_t* out, const uint64_t* a, const uint64_t* b, uint64_t batch,
+                            uint32_t limb_begin, uint32_t num_limbs, hipStream_t s) {
+  switch (p->logn) {
+#define NNTT_CHAIN(L) \
+  case L:             \
+    return launch_chain<A, L>(p, out, a, b, batch, limb_begin, num_limbs, s);
+    NNTT_CHAIN(1)
+    NNTT_CHAIN(2)
+    NNTT_CHAIN(3)
+    NNTT_CHAIN(4)
+    NNTT_CHAIN(5)
+    NNTT_CHAIN(6)
+    NNTT_CHAIN(7)
+    NNTT_CHAIN(8)
+    NNTT_CHAIN(9)
+    NNTT_CHAIN(10)
+    NNTT_CHAIN(11)
+    NNTT_CHAIN(12)
+#undef NNTT_CHAIN
+    default:
+      return hipErrorNotSupported;
   }
 }
 
@@ -986,6 +1334,31 @@ hipError_t launch_intt_mac(const ntt_plan* p, uint64_t* acc, const uint64_t* ext
   if (range_is_narrow(p, 0, nqp)) return launch_mac_any<Narrow>(p, acc, ms, batch, nqp, s);
   if (range_below60(p, 0, nqp)) return launch_mac_any<Wide60>(p, acc, ms, batch, nqp, s);
   return launch_mac_any<Wide>(p, acc, ms, batch, nqp, s);
+}
+
+bool chain_supported(const ntt_plan* p) { return p->logn <= kChainMaxLogN; }
+
+hipError_t launch_ct_tensor_coeff(const ntt_plan* p, uint64_t* out, const uint64_t* a, const uint64_t* b,
+                                  uint64_t batch, uint32_t limb_begin, uint32_t num_limbs, hipStream_t s) {
+  if (!chain_supported(p)) return hipErrorNotSupported;
+  if (batch * num_limbs == 0) return hipSuccess;
+  if (range_is_narrow(p, limb_begin, num_limbs))
+    return launch_chain_any<Narrow>(p, out, a, b, batch, limb_begin, num_limbs, s);
+  if (range_below60(p, limb_begin, num_limbs))
+    return launch_chain_any<Wide60>(p, out, a, b, batch, limb_begin, num_limbs, s);
+  return launch_chain_any<Wide>(p, out, a, b, batch, limb_begin, num_limbs, s);
+}
+
+bool ks_middle_supported(const ntt_plan* p, uint32_t dnum, uint32_t chunk) {
+  return p->logn >= 15 && dnum >= 1 && dnum <= 4 && chunk >= dnum;
+}
+
+hipError_t launch_ks_middle(const ntt_plan* p, uint64_t* acc, uint64_t* ext, const uint64_t* ksk, uint64_t batch,
+                            uint32_t nqp, uint32_t dnum, hipStream_t s) {
+  if (batch == 0) return hipSuccess;
+  if (range_is_narrow(p, 0, nqp)) return launch_ks_middle_any<Narrow>(p, acc, ext, ksk, batch, nqp, dnum, s);
+  if (range_below60(p, 0, nqp)) return launch_ks_middle_any<Wide60>(p, acc, ext, ksk, batch, nqp, dnum, s);
+  return launch_ks_middle_any<Wide>(p, acc, ext, ksk, batch, nqp, dnum, s);
 }
 
 hipError_t launch_intt_mac_hoisted(const ntt_plan* p, uint64_t* acc, const uint64_t* ext, const uint64_t* ksk,

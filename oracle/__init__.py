@@ -181,6 +181,19 @@ def batch_tensor(a, b, primes) -> np.ndarray:
     return out
 
 
+def ct_tensor_coeff(a, b, primes, threads: int = 0) -> np.ndarray:
+    """Ciphertext product in the coefficient domain (the ciphertext "mul" of the
+    kestrel-llm overview's CKKS layer, section 3): a, b [..., 2, limbs, n] ->
+    [..., 3, limbs, n] with the negacyclic products d0 = a0 b0, d1 = a0 b1 + a1 b0,
+    d2 = a1 b1 mod q.  The oracle's forward NTT, slot products and inverse NTT in
+    the order the definition gives (convolution theorem), each step pinned."""
+    a, b = _u64(a), _u64(b)
+    assert a.shape == b.shape and a.shape[-3] == 2
+    fa = batch_ntt(a, primes, threads=threads)
+    fb = batch_ntt(b, primes, threads=threads)
+    return batch_ntt(batch_tensor(fa, fb, primes), primes, inverse=True, threads=threads)
+
+
 def batch_automorph(x, g: int, domain: int, primes) -> np.ndarray:
     x = _u64(x)
     out = np.zeros_like(x)

@@ -50,12 +50,15 @@ def test_keyswitch_shapes_vs_oracle(B, logn, nq, npr, dnum):
 
 
 @pytest.mark.parametrize("logn,bits,nq,npr,dnum", [(15, 60, 12, 4, 3), (15, 60, 10, 2, 5), (15, 62, 12, 4, 3),
-                                                   (15, 62, 10, 3, 5), (16, 62, 8, 2, 4), (15, 30, 6, 2, 2)])
+                                                   (15, 62, 10, 3, 5), (16, 62, 8, 2, 4), (15, 30, 6, 2, 2),
+                                                   (15, 60, 8, 4, 1), (16, 30, 6, 2, 3), (15, 30, 8, 3, 4)])
 def test_keyswitch_fused_product_paths(B, logn, bits, nq, npr, dnum):
-    """Two-pass ring sizes, where the key product runs inside the inverse transform:
-    both splits (2^15 = 2^7 x 2^8, 2^16), compile-time digit counts and the runtime
-    loop (dnum 5), 60-bit (one reduction) and 62-bit primes (four products per
-    reduction, so five digits take two), and 30-bit primes."""
+    """Two-pass ring sizes, where one kernel runs the forward row pass of every digit,
+    the key product and the inverse row pass (dnum 1..4), or, for more digits, the key
+    product rides on the inverse transform's row pass: both splits (2^15 = 2^7 x 2^8,
+    2^16), every compile-time digit count and the runtime loop (dnum 5), 60-bit (one
+    reduction) and 62-bit primes (four products per reduction, so five digits take
+    two), and 30-bit primes."""
     n = 1 << logn
     qp = list(primes(bits, 2 * n, nq + npr))
     plan = B.Plan(n, qp, 0)
@@ -262,3 +265,24 @@ def test_explicit_side_stream_without_workspace(B, as_int):
     announce("count_noncanonical on a side stream", as_int)
     assert B.count_noncanonical(plan, dbad.view(-1, nq, n), stream=stream) == 2
     assert B.count_noncanonical(plan, dct.view(-1, nq, n), stream=stream) == 0
+
+
+def test_keyswitch_middle_split_under_launch_cap(B):
+    """Under a launch cap that admits one ciphertext's transforms per launch, the fused
+    middle of a 2^15 key-switch (forward column pass, fused row kernel, inverse column
+    pass) runs in parts: three ciphertexts against the oracle."""
+    n, nq, npr, dnum, g = 1 << 15, 4, 2, 2, 5
+    qp = list(primes(60, 2 * n, nq + npr))
+    plan = B.Plan(n, qp, 0)
+    ks = B.KeySwitchPlan(plan, nq, npr, dnum)
+    ct = residues((3, 2, nq, n), qp[:nq], 9420)
+    ksk = residues((dnum, 2, nq + npr, n), qp, 9421)
+    # the largest of the three launches is a column pass over dnum x 6 limbs: 16 blocks
+    # of 256 threads per limb
+    B.set_max_launch_threads(dnum * (nq + npr) * 16 * 256)
+    try:
+        announce("keyswitch middle under a launch cap")
+        out = host(B.keyswitch(ks, dev(np.zeros_like(ct)), dev(ct), dev(ksk), g))
+    finally:
+        B.set_max_launch_threads(0)
+    assert_bits_equal(out, orc.keyswitch(ct, ksk, g, qp, nq, dnum), "keyswitch middle in parts")

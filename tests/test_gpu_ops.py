@@ -109,6 +109,63 @@ def test_tensor_limb_subrange(B):
     assert_bits_equal(host(d), orc.batch_tensor(a, b, sub), "tensor limbs 2..4")
 
 
+def test_ct_tensor_coeff_chain_workload(B):
+    """The inner chain (n = 2048, 112 primes of 30 bits, 4 tokens x 2 components) as one
+    coefficient-domain ciphertext product, against the oracle's NTT, tensor and INTT."""
+    w = workloads.CHAIN
+    ps = list(primes(w.bits, 2 * w.n, w.limbs))
+    a = residues(w.shape_a, ps, w.seed_a)
+    b = residues(w.shape_a, ps, w.seed_b)
+    import torch
+    out = torch.empty((w.shape_a[0], 3) + tuple(w.shape_a[2:]), dtype=torch.int64, device="cuda:0")
+    announce("ct_tensor_coeff chain workload")
+    B.ct_tensor_coeff(B.Plan(w.n, ps, 0), out, dev(a), dev(b))
+    assert_bits_equal(host(out), orc.ct_tensor_coeff(a, b, ps), "ct_tensor_coeff chain")
+
+
+@pytest.mark.parametrize("bits", [30, 60, 62])
+def test_ct_tensor_coeff_sweep(B, bits):
+    """Every supported ring (n = 2 .. 4096), a ragged batch of 3 ciphertexts."""
+    import torch
+    for logn in range(1, 13):
+        n = 1 << logn
+        ps = list(primes(bits, 1 << 17, 3))  # 1 mod 2^17 covers every n here
+        a = residues((3, 2, 3, n), ps, 9300 + logn)
+        b = residues((3, 2, 3, n), ps, 9350 + logn)
+        out = torch.empty((3, 3, 3, n), dtype=torch.int64, device="cuda:0")
+        announce("ct_tensor_coeff sweep", bits, logn)
+        B.ct_tensor_coeff(B.Plan(n, ps, 0), out, dev(a), dev(b))
+        assert_bits_equal(host(out), orc.ct_tensor_coeff(a, b, ps), f"ct_tensor_coeff bits={bits} logn={logn}")
+
+
+def test_ct_tensor_coeff_subrange_and_validation(B):
+    import ctypes
+    import torch
+    n = 1 << 11
+    ps = list(primes(30, 2 * n, 4)) + list(primes(60, 2 * n, 4))
+    plan = B.Plan(n, ps, 0)
+    a = residues((2, 2, 3, n), ps[3:6], 9361)  # limbs 3..5: one 30-bit and two 60-bit primes
+    b = residues((2, 2, 3, n), ps[3:6], 9362)
+    out = torch.empty((2, 3, 3, n), dtype=torch.int64, device="cuda:0")
+    announce("ct_tensor_coeff subrange")
+    B.ct_tensor_coeff(plan, out, dev(a), dev(b), limb_begin=3)
+    assert_bits_equal(host(out), orc.ct_tensor_coeff(a, b, ps[3:6]), "ct_tensor_coeff subrange")
+    L, V = B.lib(), ctypes.c_void_p
+    ta = dev(a)
+    assert L.ct_tensor_coeff(plan.handle, V(ta.data_ptr()), V(ta.data_ptr()), V(ta.data_ptr()), 2, 3, 3,
+                             None) == B.NTT_EOVERLAP
+    assert L.ct_tensor_coeff(plan.handle, V(out.data_ptr() + 8), V(ta.data_ptr()), V(ta.data_ptr()), 2, 3, 3,
+                             None) == B.NTT_EINVAL
+    assert L.ct_tensor_coeff(plan.handle, V(out.data_ptr()), V(ta.data_ptr()), V(ta.data_ptr()), 2, 6, 3,
+                             None) == B.NTT_EINVAL  # limbs beyond the plan
+    big = B.Plan(1 << 13, list(primes(30, 1 << 14, 1)), 0)
+    x = torch.zeros((1, 2, 1, 1 << 13), dtype=torch.int64, device="cuda:0")
+    y = torch.zeros((1, 3, 1, 1 << 13), dtype=torch.int64, device="cuda:0")
+    assert L.ct_tensor_coeff(big.handle, V(y.data_ptr()), V(x.data_ptr()), V(x.data_ptr()), 1, 0, 1,
+                             None) == B.NTT_EUNSUPPORTED
+    torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("domain", [0, 1])
 def test_automorph_ring_workload_all_galois(B, domain):
     w = workloads.RING
@@ -264,6 +321,9 @@ def _cap_case(B, logn):
         td = torch.empty((batch, 3, L, n), dtype=torch.int64, device=ta.device)
         B.ct_tensor_ntt(plan, td, ta, tb)
         assert_bits_equal(host(td), orc.batch_tensor(fa, fb, ps), "tensor")
+        tcc = torch.empty((batch, 3, L, n), dtype=torch.int64, device=ta.device)
+        B.ct_tensor_coeff(plan, tcc, dev(a), dev(b))
+        assert_bits_equal(host(tcc), orc.ct_tensor_coeff(a, b, ps), "coefficient-domain product")
         B.ntt_inverse(plan, ta)
         assert_bits_equal(host(ta), a, "inverse")
         for domain in (0, 1):

@@ -271,6 +271,24 @@ def test_tensor_karatsuba_and_schoolbook(primes):
             assert [int(v) for v in orc.ntt_inverse(d[bi, 1, l], q, psi)] == [int(v) for v in want]
 
 
+def test_ct_tensor_coeff_is_the_negacyclic_product(primes):
+    """The coefficient-domain ciphertext product: every output polynomial against the
+    schoolbook negacyclic products, on 30- and 60-bit primes and two ring sizes."""
+    for bits, n in ((30, 32), (60, 128)):
+        ps = orc.find_primes(bits, 2 * n, 3)
+        a = inputs.uniform_residues((2, 2, 3, n), ps, 91 + n)
+        b = inputs.uniform_residues((2, 2, 3, n), ps, 92 + n)
+        d = orc.ct_tensor_coeff(a, b, ps)
+        assert d.shape == (2, 3, 3, n)
+        for bi in range(2):
+            for l, q in enumerate(ps):
+                a0, a1, b0, b1 = a[bi, 0, l], a[bi, 1, l], b[bi, 0, l], b[bi, 1, l]
+                assert np.array_equal(d[bi, 0, l], orc.schoolbook(a0, b0, q))
+                want1 = (orc.schoolbook(a0, b1, q).astype(object) + orc.schoolbook(a1, b0, q).astype(object)) % q
+                assert [int(v) for v in d[bi, 1, l]] == [int(v) for v in want1]
+                assert np.array_equal(d[bi, 2, l], orc.schoolbook(a1, b1, q))
+
+
 def int_(x):
     return [int(v) for v in x]
 
