@@ -53,15 +53,15 @@ def code_text(source: str) -> str:
 
 
 def kernel_sources_digest(read=None):
-    """sha256/16 over the code text of modarith.h + ntt.hip (comments excluded, so a
-    comment edit does not invalidate counters taken on the same kernels)."""
+    """sha256/16 over the code text of modarith.h + ntt_passes.h + ntt.hip (comments
+    excluded, so a comment edit does not invalidate counters taken on the same kernels)."""
     import hashlib
     if read is None:
         def read(name):
             with open(os.path.join(ROOT, "negacyclic_ntt_amd", "csrc", name)) as fh:
                 return fh.read()
     h = hashlib.sha256()
-    for f in ("modarith.h", "ntt.hip"):
+    for f in ("modarith.h", "ntt_passes.h", "ntt.hip"):
         h.update(code_text(read(f)).encode())
     return h.hexdigest()[:16]
 
@@ -69,7 +69,7 @@ def kernel_sources_digest(read=None):
 def recorded_fields(name):
     """The `- key: value` fields of a committed counter summary under profiles/, if it
     was taken on the current kernel sources (its kernel_sources_sha256_16 matches the
-    code text of modarith.h + ntt.hip); else {}."""
+    code text of modarith.h + ntt_passes.h + ntt.hip); else {}."""
     path = os.path.join(PROFILES, name)
     if not os.path.exists(path):
         return {}
