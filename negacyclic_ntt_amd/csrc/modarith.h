@@ -192,6 +192,19 @@ __device__ __forceinline__ uint64_t barrett_mul(uint64_t a, uint64_t c, const Ba
   return barrett_reduce(__umul64hi(a, c), a * c, b);
 }
 
+// The same for q < 2^30 (k <= 30): the product x y < 2^(2k) fits 64 bits, q1 < 2^(k+1)
+// and q1 mu < 2^62, so the whole reduction is 64-bit arithmetic of 32-bit operands;
+// x y - q3 q lies in [0, 3q) < 2^32.
+__device__ __forceinline__ uint32_t barrett_mul_narrow(uint32_t x, uint32_t y, const Barrett& b) {
+  const uint64_t p = (uint64_t)x * y;
+  const uint64_t q1 = p >> (b.k - 1);
+  const uint64_t q3 = (q1 * b.mu) >> (b.k + 1);
+  uint32_t r = (uint32_t)(p - q3 * b.q);
+  const uint32_t q = (uint32_t)b.q;
+  r = csub(r, q);
+  return csub(r, q);
+}
+
 // Exact 128-bit accumulation of 64 x 64-bit products, and Montgomery reduction with
 // R = 2^64: for T = hi 2^64 + lo < q 2^64 and ninv = -q^-1 mod 2^64, m = lo ninv
 // makes T + m q divisible by 2^64; the quotient hi + hi64(m q) + [lo != 0] equals

@@ -208,9 +208,17 @@ __global__ __launch_bounds__(ChainCfg<LOGN>::NT) void ct_tensor_coeff_kernel(
     const int o = lpos<A>(k);
     const uint64_t x0 = finish<A, true>(lds[o], m), x1 = finish<A, true>(lds[STRIDE + o], m);
     const uint64_t y0 = finish<A, true>(lds[2 * STRIDE + o], m), y1 = finish<A, true>(lds[3 * STRIDE + o], m);
-    lds[o] = (T)barrett_mul(x0, y0, br);
-    lds[STRIDE + o] = (T)add_mod(barrett_mul(x0, y1, br), barrett_mul(x1, y0, br), br.q);
-    lds[2 * STRIDE + o] = (T)barrett_mul(x1, y1, br);
+    if constexpr (A::kShoupBits == 32) {  // q < 2^30
+      const uint32_t q32 = (uint32_t)br.q;
+      lds[o] = barrett_mul_narrow((uint32_t)x0, (uint32_t)y0, br);
+      lds[STRIDE + o] = csub(barrett_mul_narrow((uint32_t)x0, (uint32_t)y1, br) +
+                                 barrett_mul_narrow((uint32_t)x1, (uint32_t)y0, br), q32);
+      lds[2 * STRIDE + o] = barrett_mul_narrow((uint32_t)x1, (uint32_t)y1, br);
+    } else {
+      lds[o] = (T)barrett_mul(x0, y0, br);
+      lds[STRIDE + o] = (T)add_mod(barrett_mul(x0, y1, br), barrett_mul(x1, y0, br), br.q);
+      lds[2 * STRIDE + o] = (T)barrett_mul(x1, y1, br);
+    }
   }
   __syncthreads();
   {
