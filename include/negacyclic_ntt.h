@@ -283,7 +283,7 @@ int keyswitch_noalloc(const ntt_ks_plan *plan, uint64_t *out, const uint64_t *ct
                       uint64_t galois_elt, uint64_t batch, void *stream);
 
 /* Bytes of device workspace keyswitch_hoisted needs for num_rot rotations of `batch`
- * ciphertexts: batch * (dnum + 2 num_rot) * (num_q + num_p) * n * 8 (caller-owned,
+ * ciphertexts: batch * ((dnum + 2 num_rot) * (num_q + num_p) + num_q) * n * 8 (caller-owned,
  * as for keyswitch_workspace_size).  NTT_EINVAL for num_rot 0, NTT_EUNSUPPORTED for
  * num_rot > 64 or batch > 4096. */
 int keyswitch_hoisted_workspace_size(const ntt_ks_plan *plan, uint32_t num_rot, uint64_t batch, size_t *bytes);

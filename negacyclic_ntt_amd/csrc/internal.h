@@ -150,9 +150,13 @@ hipError_t launch_ks_middle(const ntt_plan* p, uint64_t* acc, uint64_t* ext, con
                             uint32_t nqp, uint32_t dnum, hipStream_t s);
 // The same for hoisted rotations: acc [num_rot][batch][2][nqp][n] from the shared digits
 // gathered through each rotation's slot permutation, keys [num_rot][dnum][2][nqp][n].
+// c0hat (nullable): NTT(c0) [batch][nq][n]; with it component 0 also sums P * NTT(c0)
+// through the rotation's slot permutation (pr64[t] = P 2^64 mod q_t, t < nq), which then
+// takes chunk > dnum (one more product per reduction).
 hipError_t launch_intt_mac_hoisted(const ntt_plan* p, uint64_t* acc, const uint64_t* ext, const uint64_t* ksk,
                                    uint64_t batch, uint32_t num_rot, uint32_t nqp, uint32_t dnum, uint32_t chunk,
-                                   const HoistArgs& ha, hipStream_t s);
+                                   const HoistArgs& ha, const uint64_t* c0hat, const uint64_t* pr64, uint32_t nq,
+                                   hipStream_t s);
 // True when every prime in [limb_begin, limb_begin + num_limbs) is below 2^30.
 bool range_is_narrow(const ntt_plan* p, uint32_t limb_begin, uint32_t num_limbs);
 // True when every prime in the range is below 2^60.

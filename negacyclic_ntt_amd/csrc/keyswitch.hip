@@ -365,6 +365,7 @@ struct ntt_ks_plan {
   const ntt_plan* qp = nullptr;
   uint32_t nq = 0, np = 0, dnum = 0, alpha = 0;
   uint32_t mac_chunk = 1;  // products summed before a Montgomery reduction: chunk q < 2^64
+  uint32_t mac_chunk_max = 1;  // the same bound without the cap at dnum (at most 64)
   bool below60 = false;    // every prime of Q u P below 2^60
   void* d_const = nullptr;
   KsDev dev{};
@@ -414,6 +415,7 @@ extern "C" int keyswitch_plan_create(ntt_ks_plan** out, const ntt_plan* qp, uint
   std::vector<uint64_t> moduli(m, m + nqp);
   std::vector<Tw> dg((size_t)dnum * K * K, Tw{0, 0}), de((size_t)dnum * nqp * K, Tw{0, 0});
   std::vector<Tw> pg((size_t)KP * KP, Tw{0, 0}), pe((size_t)nq * KP, Tw{0, 0}), pinv(nq), rs(nqp);
+  std::vector<uint64_t> pr64(nq);
   uint64_t qmax = 0;
   for (uint32_t t = 0; t < nqp; ++t) {
     rs[t] = shoup_pair((uint64_t)(((unsigned __int128)1 << 64) % m[t]), m[t]);  // 2^64 mod q_t
@@ -457,17 +459,20 @@ extern "C" int keyswitch_plan_create(ntt_ks_plan** out, const ntt_plan* qp, uint
     uint64_t P = 1;
     for (uint32_t i = 0; i < np_; ++i) P = host_mulmod(P, m[nq + i] % m[l], m[l]);
     pinv[l] = shoup_pair(host_invmod(P, m[l]), m[l]);
+    pr64[l] = host_mulmod(P, rs[l].w, m[l]);  // P 2^64 mod q_l
   }
 
   const size_t sz_m = moduli.size() * 8, sz_dg = dg.size() * sizeof(Tw), sz_de = de.size() * sizeof(Tw);
   const size_t sz_pg = pg.size() * sizeof(Tw), sz_pe = pe.size() * sizeof(Tw), sz_pi = pinv.size() * sizeof(Tw);
   const size_t sz_rs = rs.size() * sizeof(Tw), sz_d30 = de30.size() * sizeof(C30), sz_p30 = pe30.size() * sizeof(C30);
   const size_t sz_ni = ninv.size() * 8, sz_dg30 = dg30.size() * sizeof(C30), sz_pg30 = pg30.size() * sizeof(C30);
+  const size_t sz_pr = pr64.size() * 8;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  constexpr int kParts = 12;
-  const void* src[kParts] = {moduli.data(), dg.data(),   de.data(),   pg.data(), pe.data(),   pinv.data(),
-                             rs.data(),     de30.data(), pe30.data(), ninv.data(), dg30.data(), pg30.data()};
-  const size_t sz[kParts] = {sz_m, sz_dg, sz_de, sz_pg, sz_pe, sz_pi, sz_rs, sz_d30, sz_p30, sz_ni, sz_dg30, sz_pg30};
+  constexpr int kParts = 13;
+  const void* src[kParts] = {moduli.data(), dg.data(),   de.data(),   pg.data(),   pe.data(),   pinv.data(), rs.data(),
+                             de30.data(),   pe30.data(), ninv.data(), dg30.data(), pg30.data(), pr64.data()};
+  const size_t sz[kParts] = {sz_m,   sz_dg,  sz_de, sz_pg,   sz_pe,   sz_pi, sz_rs,
+                             sz_d30, sz_p30, sz_ni, sz_dg30, sz_pg30, sz_pr};
   size_t total = 0;
   for (int i = 0; i < kParts; ++i) total += al(sz[i]);
   std::vector<uint8_t> blob(total, 0);
@@ -515,7 +520,9 @@ extern "C" int keyswitch_plan_create(ntt_ks_plan** out, const ntt_plan* qp, uint
   p->dev.ninv = (const uint64_t*)(base + off[9]);
   p->dev.digit_garner30 = (const C30*)(base + off[10]);
   p->dev.p_garner30 = (const C30*)(base + off[11]);
+  p->dev.p_r64 = (const uint64_t*)(base + off[12]);
   p->mac_chunk = (uint32_t)std::min<uint64_t>(dnum, ~0ull / qmax);
+  p->mac_chunk_max = (uint32_t)std::min<uint64_t>(64, ~0ull / qmax);
   *out = p;
   return NTT_OK;
 }
@@ -637,7 +644,9 @@ int ks_moddown(const ntt_ks_plan* p, uint64_t* out, const uint64_t* acc, const K
                uint32_t num_rot, uint64_t batch, hipStream_t s) {
   const uint32_t n = p->qp->n, nq = p->nq, nqp = nq + p->np;
   const uint32_t tiles = (n + kKsThreads - 1) / kKsThreads;
-  const uint32_t groups = std::max(1u, std::min(kModDownGroups, nq));
+  // Groups of output primes recompute the Garner digits over P but add waves: they pay
+  // for one ciphertext; several rotations or ciphertexts fill the GPU with one group.
+  const uint32_t groups = (uint64_t)num_rot * batch >= 4 ? 1u : std::max(1u, std::min(kModDownGroups, nq));
   const uint64_t out_rot = batch * 2 * nq * n, acc_rot = batch * 2 * nqp * n;
   const uint64_t down_chunk = kMaxGridY / 2;
   for (uint64_t b0 = 0; b0 < batch; b0 += down_chunk) {
@@ -735,8 +744,8 @@ extern "C" int keyswitch_hoisted_workspace_size(const ntt_ks_plan* p, uint32_t n
                                                size_t* bytes) {
   if (!p || !bytes || num_rot == 0) return NTT_EINVAL;
   if (batch > 4096 || num_rot > kMaxHoisted) return NTT_EUNSUPPORTED;
-  const uint64_t qplane = (uint64_t)(p->nq + p->np) * p->qp->n;
-  *bytes = (size_t)(batch * (p->dnum + 2ull * num_rot) * qplane * 8);
+  const uint64_t qplane = (uint64_t)(p->nq + p->np) * p->qp->n, plane = (uint64_t)p->nq * p->qp->n;
+  *bytes = (size_t)(batch * ((p->dnum + 2ull * num_rot) * qplane + plane) * 8);
   return NTT_OK;
 }
 
@@ -755,7 +764,7 @@ extern "C" int keyswitch_hoisted(const ntt_ks_plan* p, uint64_t* out, const uint
   if (((uintptr_t)out | (uintptr_t)ct | (uintptr_t)ksk) & 15u) return NTT_EINVAL;
   if ((uintptr_t)workspace & 255u) return NTT_EINVAL;
   const uint64_t plane = (uint64_t)nq * n, qplane = (uint64_t)nqp * n;
-  const uint64_t need = batch * (dnum + 2ull * num_rot) * qplane * 8;
+  const uint64_t need = batch * ((dnum + 2ull * num_rot) * qplane + plane) * 8;
   if (workspace_bytes < need) return NTT_EINVAL;
   const uint64_t ct_bytes = batch * 2 * plane * 8, out_bytes = num_rot * ct_bytes;
   const uint64_t ksk_bytes = (uint64_t)num_rot * dnum * 2 * qplane * 8;
@@ -776,14 +785,26 @@ extern "C" int keyswitch_hoisted(const ntt_ks_plan* p, uint64_t* out, const uint
   }
   uint64_t* ext = (uint64_t*)workspace;
   uint64_t* acc = ext + batch * (uint64_t)dnum * qplane;
+  uint64_t* c0hat = acc + batch * 2ull * num_rot * qplane;  // [batch][nq][n]
   const KsIo io{ct + plane, 2 * plane, ct, 2 * plane, 1u, ct_bytes, ct};
   rc = ks_modup(p, ext, io, 1, batch, s);  // no automorphism: the digits are shared
   if (rc) return rc;
   if (launch_ntt(qp, ext, batch * dnum, 0, nqp, false, s) != hipSuccess) return NTT_EDEVICE;
   if (intt_mac_supported(qp)) {  // key products fused into the inverse transform's first pass
-    if (launch_intt_mac_hoisted(qp, acc, ext, ksk, batch, num_rot, nqp, dnum, p->mac_chunk, ha, s) != hipSuccess)
+    // Every rotation adds sigma_g(c0) to its output: as P sigma_g(c0), a slot permutation
+    // of P NTT(c0), it joins the key product, and ModDown runs without a gather.
+    const bool fold = dnum <= 4 && p->mac_chunk_max > dnum;
+    if (fold)
+      for (uint64_t b = 0; b < batch; ++b)
+        if (launch_ntt_galois(qp, c0hat + b * plane, ct + b * 2 * plane, 1, 1, 0, nq, s) != hipSuccess)
+          return NTT_EDEVICE;
+    if (launch_intt_mac_hoisted(qp, acc, ext, ksk, batch, num_rot, nqp, dnum,
+                                fold ? p->mac_chunk_max : p->mac_chunk, ha, fold ? c0hat : nullptr, p->dev.p_r64,
+                                nq, s) != hipSuccess)
       return NTT_EDEVICE;
-    return ks_moddown(p, out, acc, io, ha, num_rot, batch, s);
+    KsIo down = io;
+    if (fold) down.add_mask = 0;
+    return ks_moddown(p, out, acc, down, ha, num_rot, batch, s);
   }
   const uint32_t seglog = std::min(qp->logn, 9u);
   const dim3 grid((nqp << (qp->logn - seglog)), (uint32_t)batch);

@@ -421,6 +421,14 @@ struct MacSrc {
   const uint64_t* ext;  // [batch][dnum][nqp][n]
   const uint64_t* ksk;  // [dnum][2][nqp][n]
   uint32_t dnum, chunk;
+  // Hoisted rotations only (nullptr otherwise): NTT(c0) [batch][nq][n] and, per prime of
+  // Q, P 2^64 mod q.  Component 0 of every Q prime then also sums P * NTT(c0) at the
+  // rotation's slots, i.e. P sigma_g(c0) in the NTT domain, so that ModDown yields
+  // sigma_g(c0) + ModDown(acc_0) with no additive input (floor((X + P Y) / P) equals
+  // floor(X / P) + Y for every integer Y, and Q vanishes modulo each q).
+  const uint64_t* c0hat;
+  const uint64_t* pr64;
+  uint32_t nq;
 };
 
 // Key residues are read once per launch: non-temporal loads keep them from evicting
@@ -681,6 +689,9 @@ __global__ __launch_bounds__(RowCfg<LOGN2>::NT) void ntt_row_mac_hoisted_kernel(
   const uint64_t* kk = ms.ksk + (((uint64_t)rot * ms.dnum * 2 + (poly & 1)) * nqp + t) * (uint64_t)N + off;
   const ModInfo& m = mods[t];
   const uint64_t q = m.q, ninv = m.mont_ninv;
+  const bool fold = DN > 0 && ms.c0hat != nullptr && (poly & 1) == 0 && t < ms.nq;
+  const uint64_t* cz = fold ? ms.c0hat + (b * ms.nq + t) * (uint64_t)N : nullptr;
+  const uint64_t pr = fold ? ms.pr64[t] : 0;
 
   constexpr int kIters = (kRows * N2) / (2 * NT);
   static_assert((kRows * N2) % (2 * NT) == 0, "whole iterations");
@@ -700,10 +711,19 @@ __global__ __launch_bounds__(RowCfg<LOGN2>::NT) void ntt_row_mac_hoisted_kernel(
         d1[j] = xe[j * plane + s1];
         k[j] = load_key(kk + 2 * j * plane + e);
       }
+      uint64_t z0 = 0, z1 = 0;
+      if (fold) {
+        z0 = cz[s0];
+        z1 = cz[s1];
+      }
 #pragma unroll
       for (int j = 0; j < DN; ++j) {
         mac128(a0, d0[j], k[j].x);
         mac128(a1, d1[j], k[j].y);
+      }
+      if (fold) {  // DN + 1 products: the launcher checks (DN + 1) q < 2^64
+        mac128(a0, z0, pr);
+        mac128(a1, z1, pr);
       }
       r0 = csub(redc(a0, q, ninv), q);
       r1 = csub(redc(a1, q, ninv), q);
@@ -1050,7 +1070,7 @@ hipError_t launch_intt_mac(const ntt_plan* p, uint64_t* acc, const uint64_t* ext
                            uint32_t nqp, uint32_t dnum, uint32_t chunk, hipStream_t s) {
   if (!intt_mac_supported(p)) return hipErrorNotSupported;
   if (batch == 0) return hipSuccess;
-  const MacSrc ms{ext, ksk, dnum, chunk};
+  const MacSrc ms{ext, ksk, dnum, chunk, nullptr, nullptr, 0};
   if (range_is_narrow(p, 0, nqp)) return launch_mac_any<Narrow>(p, acc, ms, batch, nqp, s);
   if (range_below60(p, 0, nqp)) return launch_mac_any<Wide60>(p, acc, ms, batch, nqp, s);
   return launch_mac_any<Wide>(p, acc, ms, batch, nqp, s);
@@ -1083,10 +1103,13 @@ hipError_t launch_ks_middle(const ntt_plan* p, uint64_t* acc, uint64_t* ext, con
 
 hipError_t launch_intt_mac_hoisted(const ntt_plan* p, uint64_t* acc, const uint64_t* ext, const uint64_t* ksk,
                                    uint64_t batch, uint32_t num_rot, uint32_t nqp, uint32_t dnum, uint32_t chunk,
-                                   const HoistArgs& ha, hipStream_t s) {
+                                   const HoistArgs& ha, const uint64_t* c0hat, const uint64_t* pr64, uint32_t nq,
+                                   hipStream_t s) {
   if (!intt_mac_supported(p)) return hipErrorNotSupported;
   if (batch == 0) return hipSuccess;
-  const MacSrc ms{ext, ksk, dnum, chunk};
+  // the folded term is one more product per reduction, in the compile-time digit counts
+  if (c0hat && (dnum >= chunk || dnum > 4)) return hipErrorInvalidValue;
+  const MacSrc ms{ext, ksk, dnum, chunk, c0hat, pr64, nq};
   if (range_is_narrow(p, 0, nqp)) return launch_mac_hoisted_any<Narrow>(p, acc, ms, batch, num_rot, nqp, ha, s);
   if (range_below60(p, 0, nqp)) return launch_mac_hoisted_any<Wide60>(p, acc, ms, batch, num_rot, nqp, ha, s);
   return launch_mac_hoisted_any<Wide>(p, acc, ms, batch, num_rot, nqp, ha, s);

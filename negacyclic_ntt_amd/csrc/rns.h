@@ -151,6 +151,7 @@ struct KsDev {
   const Tw* p_garner;       // [KP][KP]       (KP = kMaxSpecial)
   const Tw* p_eval;         // [nq][KP]
   const Tw* p_inv;          // [nq]
+  const uint64_t* p_r64;    // [nq]     P 2^64 mod q_l (hoisted rotations fold P sigma_g(c0) into the key product)
   const Tw* r_scale;        // [nq+np]  2^64 mod q_t
   const C30* digit_eval30;  // [dnum][nq+np][K]  below 2^60: digit products times 2^128 mod q_t
   const C30* p_eval30;      // [nq][KP]           below 2^60: products of P's primes times 2^64
