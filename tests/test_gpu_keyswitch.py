@@ -37,7 +37,7 @@ def test_keyswitch_workload_vs_oracle(B, g):
 
 
 @pytest.mark.parametrize("logn,nq,npr,dnum", [(10, 24, 8, 3), (12, 6, 2, 2), (11, 16, 16, 1), (3, 4, 3, 4),
-                                              (13, 12, 5, 3)])
+                                              (13, 12, 5, 3), (14, 9, 4, 3)])
 def test_keyswitch_shapes_vs_oracle(B, logn, nq, npr, dnum):
     n = 1 << logn
     qp, plan, ks = _setup(B, n, nq, npr, dnum)

@@ -151,6 +151,26 @@ def test_ntt_forward_galois_sweep(B, logn):
         assert_bits_equal(host(out), want, f"NTT(sigma_{g}) n=2^{logn}")
 
 
+@pytest.mark.parametrize("bits", [60, 62])
+@pytest.mark.parametrize("logn", [13, 14])
+def test_ntt_forward_galois_wide(B, logn, bits):
+    # 64-bit residues where the transform changes shape (one row per workgroup at 2^13,
+    # the two-pass split of the forward at 2^14), out of place and in place
+    import torch
+    n = 1 << logn
+    ps = _prime_set(bits)
+    plan = B.Plan(n, ps, 0)
+    x = residues((3, 3, n), ps, 7800 + logn + bits)
+    tx = dev(x)
+    out = torch.empty_like(tx)
+    for g in (3, 5, 2 * n - 1):
+        announce("ntt_forward_galois wide", logn, bits, g)
+        B.ntt_forward_galois(plan, out, tx, g)
+        assert_bits_equal(host(out), orc.batch_ntt(orc.batch_automorph(x, g, 0, ps), ps), f"NTT(sigma_{g})")
+    B.ntt_forward_galois(plan, tx, tx, 25)
+    assert_bits_equal(host(tx), orc.batch_ntt(orc.batch_automorph(x, 25, 0, ps), ps), "in place")
+
+
 @pytest.mark.parametrize("w", [workloads.CHAIN, workloads.RING], ids=lambda w: w.name)
 def test_ntt_forward_galois_workload_in_place(B, w):
     ps = primes(w.bits, 2 * w.n, w.limbs)
