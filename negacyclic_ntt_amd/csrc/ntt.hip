@@ -972,12 +972,12 @@ hipError_t launch_any(const ntt_plan* p, uint64_t* data, const uint64_t* in, uin
     NNTT_CASE(13)
 #undef NNTT_CASE
     case 14:
-      // 64-bit residues: the forward transforms take the two-pass split (128 x 128), the
-      // inverse the whole-row kernel.  Measured on MI355X, 2048 limbs of 60 bits: forward
-      // 279-286 -> 230-240 us; the split inverse was 315-364 us against 310-334.
-      if constexpr (sizeof(typename A::T) == 8) {
-        if (op != Op::kInverse) return launch_split<A, 7, 7>(p, data, in, rows, limb_begin, num_limbs, op, g, s);
-      }
+      // 64-bit residues take the two-pass split (128 x 128): with one 136 KiB whole-row
+      // workgroup per CU nothing overlaps a row's loads and stores.  Measured on MI355X,
+      // 2048 limbs of 60 bits: forward 279-286 -> 230-240 us, inverse 292-296 -> 245 us.
+      // 30-bit rows (68 KiB, two workgroups per CU) keep the whole-row kernel.
+      if constexpr (sizeof(typename A::T) == 8)
+        return launch_split<A, 7, 7>(p, data, in, rows, limb_begin, num_limbs, op, g, s);
       return launch_lds<A, 14>(p, data, in, rows, limb_begin, num_limbs, op, g, s);
     case 15:
       return launch_split<A, 7, 8>(p, data, in, rows, limb_begin, num_limbs, op, g, s);

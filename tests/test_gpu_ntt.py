@@ -155,7 +155,7 @@ def test_ntt_forward_galois_sweep(B, logn):
 @pytest.mark.parametrize("logn", [13, 14])
 def test_ntt_forward_galois_wide(B, logn, bits):
     # 64-bit residues where the transform changes shape (one row per workgroup at 2^13,
-    # the two-pass split of the forward at 2^14), out of place and in place
+    # the two-pass split at 2^14), out of place and in place
     import torch
     n = 1 << logn
     ps = _prime_set(bits)
