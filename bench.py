@@ -581,14 +581,15 @@ def main():
 
     rows = ["ntt_forward", "poly_mul_ntt", "ct_tensor_ntt", "ntt_inverse", "automorph", "keyswitch"]
     ev = {r: [] for r in rows}
+    # One event between consecutive rows, across steps too (6 markers per step and one
+    # before the first timed row): row i is timed from the event before it to the event
+    # after it, on the stream the library uses.  A fresh event at the start of every step
+    # put two markers (~10 us of idle GPU) in front of each step's forward NTT.
+    last = [None]
 
     def step(s, timed):
         a, b = sets[s % len(sets)]
         g = galois[s % len(galois)]
-
-        # One event between consecutive rows (7 markers per step): row i is timed from
-        # the event before it to the event after it, on the stream the library uses.
-        last = [None]
 
         def run(name, fn):
             if timed:

@@ -16,7 +16,7 @@
 //      kernel per row tile runs the forward row pass of every digit, the key product
 //      and the inverse row pass (ntt.hip, ntt_row_ks_kernel), between the two column
 //      passes; with more digits the key product rides on the inverse's row pass;
-//      smaller rings use mac_kernel between whole-row transforms;
+//      smaller rings use mac_kernel between the transforms;
 //   6. ModDown (exact floor, FHElium's "QP-to-Q ModDown"):
 //      out_c = floor(X_c / P) mod q_l = (acc_c[l] - (X_c mod P)) * P^-1 mod q_l,
 //      X_c mod P from the P residues by Garner; out_0 += sigma_g(c0).

@@ -18,9 +18,11 @@
 //
 // Kernels:
 //   ntt_lds_kernel  : whole limb resident in LDS, n <= 2^14 (128 KiB of
-//                     residues fit the 160 KiB LDS of one gfx950 workgroup).
-//   ntt_col_kernel / ntt_row_kernel : the two halves for n = 2^15, 2^16; the
-//                     intermediate goes through L2/MALL/HBM between launches.
+//                     residues fit the 160 KiB LDS of one gfx950 workgroup); at
+//                     n = 2^14 only for 30-bit residues.
+//   ntt_col_kernel / ntt_row_kernel : the two halves for n = 2^15, 2^16, and for
+//                     n = 2^14 with 64-bit residues; the intermediate goes through
+//                     L2/MALL/HBM between launches.
 //   ntt_row_ks_kernel : the key-switch's middle for up to 4 digits -- the forward row
 //                     pass of every digit's row tile, the key product of both
 //                     components and the inverse row pass, the digits kept in LDS.
