@@ -245,11 +245,14 @@ def test_hoisted_shapes_vs_oracle(B, logn, nq, npr, dnum, batch):
                       orc.keyswitch_hoisted(ct, ksk, gs, qp[: nq + npr], nq, dnum), "hoisted shape")
 
 
-@pytest.mark.parametrize("bits,nq,npr,dnum", [(60, 12, 4, 3), (60, 10, 2, 5), (62, 10, 3, 5), (62, 8, 4, 2)])
+@pytest.mark.parametrize("bits,nq,npr,dnum", [(60, 12, 4, 3), (60, 10, 2, 5), (62, 10, 3, 5), (62, 8, 4, 2),
+                                               (62, 8, 4, 4)])
 def test_hoisted_fused_product_paths(B, bits, nq, npr, dnum):
     """n = 2^15: the rotations' key products run inside the inverse transform's first
     pass (compile-time and runtime digit counts; 62-bit primes take several
-    reductions per product sum)."""
+    reductions per product sum).  P sigma_g(c0) joins the product sum while one more
+    term fits its exact bound: 62-bit primes allow 4 terms per reduction, so dnum 2 folds
+    it in and dnum 4, at the bound, adds it in ModDown."""
     n = 1 << 15
     qp = list(primes(bits, 2 * n, nq + npr))
     plan = B.Plan(n, qp, 0)
