@@ -519,7 +519,8 @@ def sustained(B, calls):
     us = [round(ev[i].elapsed_time(ev[i + 1]) * 1e3, 1) for i in range(calls)]
     head, tail = us[: min(8, calls)], us[-min(10, calls):]
     return {"mode": "sustained_ntt_forward", "workload": W.name, "calls": calls, "us_per_call": us,
-            "first_calls_mean_us": round(sum(head) / len(head), 1), "last_calls_mean_us": round(sum(tail) / len(tail), 1)}
+            "first_calls_mean_us": round(sum(head) / len(head), 1),
+            "last_calls_mean_us": round(sum(tail) / len(tail), 1)}
 
 
 def main():

@@ -226,7 +226,8 @@ def ct_tensor_ntt(plan: Plan, out, a, b, limb_begin: int = 0, stream=None):
     batch, limbs = _check_tensor(a, plan, "a", lead=1)
     _check_tensor(b, plan, "b", lead=1)
     _check_tensor(out, plan, "out", lead=1)
-    if a.shape != b.shape or a.shape[-3] != 2 or out.shape[:-3] != a.shape[:-3] or out.shape[-3:] != (3, limbs, plan.n):
+    if (a.shape != b.shape or a.shape[-3] != 2 or out.shape[:-3] != a.shape[:-3]
+            or out.shape[-3:] != (3, limbs, plan.n)):
         raise ValueError("expected a, b [..., 2, L, n] and out [..., 3, L, n]")
     _check(lib().ct_tensor_ntt(plan.handle, _VP(out.data_ptr()), _VP(a.data_ptr()), _VP(b.data_ptr()), batch,
                                limb_begin, limbs, _stream_ptr(a, stream)), "ct_tensor_ntt")
@@ -239,7 +240,8 @@ def ct_tensor_coeff(plan: Plan, out, a, b, limb_begin: int = 0, stream=None):
     batch, limbs = _check_tensor(a, plan, "a", lead=1)
     _check_tensor(b, plan, "b", lead=1)
     _check_tensor(out, plan, "out", lead=1)
-    if a.shape != b.shape or a.shape[-3] != 2 or out.shape[:-3] != a.shape[:-3] or out.shape[-3:] != (3, limbs, plan.n):
+    if (a.shape != b.shape or a.shape[-3] != 2 or out.shape[:-3] != a.shape[:-3]
+            or out.shape[-3:] != (3, limbs, plan.n)):
         raise ValueError("expected a, b [..., 2, L, n] and out [..., 3, L, n]")
     _check(lib().ct_tensor_coeff(plan.handle, _VP(out.data_ptr()), _VP(a.data_ptr()), _VP(b.data_ptr()), batch,
                                  limb_begin, limbs, _stream_ptr(a, stream)), "ct_tensor_coeff")
