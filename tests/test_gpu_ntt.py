@@ -57,6 +57,25 @@ def test_limb_subrange_and_ragged_batch(B, logn):
     assert_bits_equal(host(t), x, "round trip")
 
 
+@pytest.mark.parametrize("logn", [14, 16])
+def test_forward_galois_limb_subrange(B, logn):
+    # the two-pass split with the automorphism folded in, on plan limbs 2..4 of 6 and a
+    # ragged batch, out of place and in place
+    import torch
+    n = 1 << logn
+    ps = primes(60, 1 << 17, 6)
+    plan = B.Plan(n, ps, 0)
+    sub = ps[2:5]
+    x = residues((3 if logn == 14 else 1, 3, n), sub, 8500 + logn)
+    tx = dev(x)
+    out = torch.empty_like(tx)
+    announce("galois subrange", logn)
+    B.ntt_forward_galois(plan, out, tx, 5, limb_begin=2)
+    assert_bits_equal(host(out), orc.batch_ntt(orc.batch_automorph(x, 5, 0, sub), sub), "limbs 2..4, g = 5")
+    B.ntt_forward_galois(plan, tx, tx, 2 * n - 1, limb_begin=2)
+    assert_bits_equal(host(tx), orc.batch_ntt(orc.batch_automorph(x, 2 * n - 1, 0, sub), sub), "in place, g = 2n - 1")
+
+
 def test_mixed_width_limb_range(B):
     # a 30-bit and a 60-bit prime in one call take the 64-bit path for both
     n = 1 << 11
